@@ -1,0 +1,205 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+The oracle computes out = x @ W^T in FP64 with ascending-k sums (guide ch. 1
+"The problem, the judge and the speed of light", §1.1 and §1.5). Each test
+below would fail for a plausible mistake: a wrong BF16 decode, a transposed
+operand, a dropped term, a wrong sign, a wrong summation order, a wrong slice.
+"""
+
+from fractions import Fraction
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workload import SHAPES, make_weight, make_x, bf16_bits_from_f32
+
+pytestmark = []
+
+
+def _bits(vals):
+    """BF16 bits of values that are exactly representable in BF16."""
+    a = np.asarray(vals, dtype=np.float32)
+    b = bf16_bits_from_f32(a)
+    back = (b.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(back, a), "test value not exact in bf16"
+    return b
+
+
+def _torch_decode(bits):
+    """Independent BF16 decode through torch's bfloat16 type."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.double().numpy()
+
+
+def test_bf16_decode_known_patterns(oracle_mod):
+    # 1 x 1 x 1 products with x = 1.0 expose the decode of W's bit pattern.
+    one = np.array([[0x3F80]], dtype=np.uint16)
+    cases = {
+        0x3F80: 1.0,
+        0xC000: -2.0,
+        0x4049: 3.140625,
+        0x0001: 2.0 ** -133,            # smallest BF16 subnormal
+        0x0080: 2.0 ** -126,            # smallest normal
+        0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,  # largest finite
+        0x8000: 0.0,                     # -0 decodes to zero; a sum started at +0 stays +0
+        0xBE80: -0.25,
+    }
+    for pat, val in cases.items():
+        w = np.array([[pat]], dtype=np.uint16)
+        got = oracle.matmul_bits(one, w)[0, 0]
+        assert got == val and (val == 0 or math.copysign(1, got) == math.copysign(1, val)), hex(pat)
+
+
+def test_brute_force_exact_small_integers(oracle_mod):
+    # Small integers times powers of two are exact in BF16 and their FP64 sums are
+    # exact, so the result must equal exact rational arithmetic bit for bit.
+    rng = np.random.default_rng(1234)
+    for trial in range(40):
+        m, n, k = (int(v) for v in rng.integers(1, 9, size=3))
+        xv = rng.integers(-8, 9, size=(m, k)) * (2.0 ** rng.integers(-6, 7, size=(m, k)))
+        wv = rng.integers(-8, 9, size=(n, k)) * (2.0 ** rng.integers(-6, 7, size=(n, k)))
+        got = oracle.matmul_bits(_bits(xv), _bits(wv))
+        for i in range(m):
+            for j in range(n):
+                exact = sum(Fraction(float(xv[i, q])) * Fraction(float(wv[j, q])) for q in range(k))
+                assert got[i, j] == float(exact), (trial, i, j)
+
+
+def test_brute_force_router_fp32_weights(oracle_mod):
+    # FP32 weights with 24-bit significands that BF16 cannot hold: a BF16-rounded
+    # router would miss these exact sums.
+    rng = np.random.default_rng(99)
+    for trial in range(20):
+        m, n, k = (int(v) for v in rng.integers(1, 7, size=3))
+        xv = rng.integers(-8, 9, size=(m, k)).astype(np.float64)
+        wi = rng.integers(-(2 ** 23), 2 ** 23, size=(n, k))
+        wv = (wi * 2.0 ** -20).astype(np.float32)
+        assert np.array_equal(wv.astype(np.float64), wi * 2.0 ** -20)
+        got = oracle.matmul_bits(_bits(xv), wv)
+        for i in range(m):
+            for j in range(n):
+                exact = sum(Fraction(float(xv[i, q])) * Fraction(float(wv[j, q])) for q in range(k))
+                assert got[i, j] == float(exact)
+
+
+def test_ascending_k_order(oracle_mod):
+    # Terms 2^60, -2^60, 1: ascending k gives exactly 1; reversed order gives 0.
+    x = _bits([[2.0 ** 30, 2.0 ** 30, 1.0]])
+    w = _bits([[2.0 ** 30, -(2.0 ** 30), 1.0]])
+    assert oracle.matmul_bits(x, w)[0, 0] == 1.0
+    # A transposed use of W (W[k, n]) would not even match shapes here:
+    w2 = _bits([[1.0, 2.0, 4.0], [8.0, 16.0, 32.0]])
+    x2 = _bits([[1.0, 1.0, 1.0]])
+    assert oracle.matmul_bits(x2, w2).tolist() == [[7.0, 56.0]]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 17, 64), (5, 33, 96), (13, 64, 300), (32, 40, 512)])
+def test_against_numpy_float64(oracle_mod, m, n, k):
+    rng = np.random.default_rng(m * 1000 + n)
+    xb = bf16_bits_from_f32(rng.standard_normal((m, k), dtype=np.float32))
+    wb = bf16_bits_from_f32(rng.standard_normal((n, k), dtype=np.float32))
+    xd, wd = _torch_decode(xb), _torch_decode(wb)
+    want = xd @ wd.T
+    scale = np.abs(xd) @ np.abs(wd).T
+    got = oracle.matmul_bits(xb, wb)
+    assert np.all(np.abs(got - want) <= 1e-13 * scale + 1e-300)
+
+
+def test_router_against_numpy_float64(oracle_mod):
+    rng = np.random.default_rng(7)
+    m, n, k = 9, 32, 1024
+    xb = bf16_bits_from_f32(rng.standard_normal((m, k), dtype=np.float32))
+    w = rng.standard_normal((n, k), dtype=np.float32)
+    want = _torch_decode(xb) @ w.astype(np.float64).T
+    scale = np.abs(_torch_decode(xb)) @ np.abs(w.astype(np.float64)).T
+    got = oracle.matmul_bits(xb, w)
+    assert np.all(np.abs(got - want) <= 1e-13 * scale)
+
+
+@pytest.mark.parametrize("layer", ["o", "router"])
+def test_probe_row_closed_form(oracle_mod, layer):
+    # A probe row has one nonzero entry 2^e at column k, so its output row is
+    # 2^e times weight column k, exactly (guide ch. 1 §1.5).
+    w = make_weight(layer, seed=3)
+    xs = make_x(layer, 1, seed=5, probe_variant=True)
+    (r, kk, e), = xs.probes
+    ref = oracle.reference(layer, xs.bits, w)
+    wcol = (w[:, kk].astype(np.uint32) << 16).view(np.float32) if w.dtype == np.uint16 else w[:, kk]
+    assert np.array_equal(ref[r], wcol.astype(np.float64) * 2.0 ** e)
+
+
+def test_probe_rows_in_batch(oracle_mod):
+    w = make_weight("o", seed=0)
+    xs = make_x("o", 64, seed=11, outliers=True)
+    assert len(xs.probes) == 8
+    ref = oracle.reference("o", xs.bits, w)
+    wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for r, kk, e in xs.probes:
+        assert np.array_equal(ref[r], wf[:, kk] * 2.0 ** e)
+
+
+def test_unpooler_slice_is_prefix(oracle_mod):
+    # At <= 8 tokens the unpooler returns only its first 1024 rows (guide ch. 1 §1.1).
+    w = make_weight("unpooler", seed=1)
+    for m in (1, 5, 8):
+        xs = make_x("unpooler", m, seed=2)
+        ref = oracle.reference("unpooler", xs.bits, w)
+        assert ref.shape == (m, 1024)
+        full = oracle.matmul_bits(xs.bits, w)
+        assert full.shape == (m, 8192)
+        assert np.array_equal(ref, full[:, :1024])
+    xs = make_x("unpooler", 9, seed=2)
+    assert oracle.reference("unpooler", xs.bits, w).shape == (9, 8192)
+
+
+def test_power_of_two_scaling_and_permutation(oracle_mod):
+    rng = np.random.default_rng(5)
+    m, n, k = 6, 48, 256
+    xv = rng.standard_normal((m, k), dtype=np.float32)
+    xb = bf16_bits_from_f32(xv)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    wb = bf16_bits_from_f32(rng.standard_normal((n, k), dtype=np.float32))
+    base = oracle.matmul_bits(xb, wb)
+    scaled = oracle.matmul_bits(bf16_bits_from_f32(xf * np.float32(8.0)), wb)
+    assert np.array_equal(scaled, base * 8.0)
+    perm = rng.permutation(m)
+    assert np.array_equal(oracle.matmul_bits(xb[perm], wb), base[perm])
+    wperm = rng.permutation(n)
+    assert np.array_equal(oracle.matmul_bits(xb, wb[wperm]), base[:, wperm])
+
+
+def test_linearity(oracle_mod):
+    rng = np.random.default_rng(8)
+    k = 512
+    a = rng.integers(-100, 100, size=(3, k)).astype(np.float32)
+    b = rng.integers(-100, 100, size=(3, k)).astype(np.float32)
+    wb = bf16_bits_from_f32(rng.standard_normal((20, k), dtype=np.float32))
+    ra = oracle.matmul_bits(bf16_bits_from_f32(a), wb)
+    rb = oracle.matmul_bits(bf16_bits_from_f32(b), wb)
+    rab = oracle.matmul_bits(bf16_bits_from_f32(a + b), wb)
+    assert np.allclose(rab, ra + rb, rtol=1e-12, atol=1e-10)
+
+
+def test_reference_rejects_bad_inputs(oracle_mod):
+    w = make_weight("o", seed=0)
+    with pytest.raises(ValueError):
+        oracle.reference("o", np.zeros((1, 8), np.uint16), w)
+    with pytest.raises(TypeError):
+        oracle.reference("router", np.zeros((1, 8192), np.uint16), np.zeros((256, 8192), np.uint16))
+    assert oracle.reference("o", np.zeros((0, 1024), np.uint16), w).shape == (0, 8192)
+
+
+def test_thread_count_does_not_change_bits(oracle_mod):
+    rng = np.random.default_rng(3)
+    xb = bf16_bits_from_f32(rng.standard_normal((4, 777), dtype=np.float32))
+    wb = bf16_bits_from_f32(rng.standard_normal((101, 777), dtype=np.float32))
+    nt = oracle.threads()
+    try:
+        oracle.set_threads(1)
+        one = oracle.matmul_bits(xb, wb)
+    finally:
+        oracle.set_threads(nt)
+    assert np.array_equal(one, oracle.matmul_bits(xb, wb))
