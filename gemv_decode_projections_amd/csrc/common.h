@@ -1,0 +1,74 @@
+// Shared device helpers for the gfx950 projection kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Fragment geometry of v_mfma_f32_16x16x32_bf16 as the kernels use it:
+//   A (16 x 32, weights): lane l holds row l % 16, k = 8 * (l / 16) + 0..7;
+//   B (32 x 16, tokens):  lane l holds column l % 16, the same k slots;
+//   C (16 x 16, fp32):    lane l holds column l % 16, rows 4 * (l / 16) + 0..3.
+// A dot product is independent of the order of its k terms, so any k
+// permutation shared by A and B gives the same sum; what matters is that the
+// weight repack and the activation loads agree on it.
+constexpr int kRowsPerBlock = 16;
+constexpr int kStepK = 32;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// FP32 -> BF16 bits, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Exact three-way split of eight FP32 weights into BF16 parts, w = hi + mid + lo.
+// hi keeps the top 8 significand bits (truncation), mid the next 8 of the
+// exact remainder, lo the last 8; each subtraction is exact because the
+// subtrahend is a prefix of the minuend's significand, and the last remainder
+// has at most 8 significant bits. Every product of a BF16 activation with a
+// part is exact in FP32, so the MFMA sees the weight at full FP32 precision.
+// (Values below 2^-103 in magnitude would lose bits to FP32 subnormals; the
+// router's weights are many orders of magnitude above that.)
+__device__ __forceinline__ void split3_f32(const u32x4 &w0, const u32x4 &w1, u32x4 &hi, u32x4 &mid,
+                                           u32x4 &lo)
+{
+    uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    uint32_t h[8], md[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t uh = w[e] & 0xffff0000u;
+        float r1 = __builtin_bit_cast(float, w[e]) - __builtin_bit_cast(float, uh);
+        uint32_t um = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
+        float r2 = r1 - __builtin_bit_cast(float, um);
+        h[e] = uh;
+        md[e] = um;
+        l[e] = __builtin_bit_cast(uint32_t, r2);
+    }
+    // Pack pairs: element 2j in the low half, 2j+1 in the high half.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        hi[j] = (h[2 * j] >> 16) | (h[2 * j + 1] & 0xffff0000u);
+        mid[j] = (md[2 * j] >> 16) | (md[2 * j + 1] & 0xffff0000u);
+        lo[j] = (l[2 * j] >> 16) | (l[2 * j + 1] & 0xffff0000u);
+    }
+}
+
+}  // namespace gdp

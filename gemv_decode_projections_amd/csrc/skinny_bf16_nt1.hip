@@ -1,0 +1,15 @@
+// BF16-weight skinny variants with one 16-token sub-tile.
+#include "skinny.h"
+#include "variants.h"
+
+namespace gdp {
+
+#define GDP_ENTRY(NT, RB, W, S, F) {NT, RB, W, S, F, reinterpret_cast<const void *>(&skinny_kernel<NT, RB, W, S, (F != 0)>)},
+
+const SkinnyVariant kSkinnyPartBf16Nt1[] = {
+    GDP_WAVES_SPW(GDP_ENTRY, 1, 1, 0)
+    GDP_WAVES_SPW(GDP_ENTRY, 1, 2, 0)
+};
+const int kSkinnyPartBf16Nt1Count = sizeof(kSkinnyPartBf16Nt1) / sizeof(kSkinnyPartBf16Nt1[0]);
+
+}  // namespace gdp

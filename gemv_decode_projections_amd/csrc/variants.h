@@ -1,0 +1,33 @@
+// Registry of compiled kernel variants (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace gdp {
+
+struct SkinnyVariant {
+    int nt;
+    int rb;
+    int waves;
+    int spw;
+    int f32w;
+    const void *fn;   // __global__ void (SkinnyArgs)
+};
+
+// Each part is defined in its own translation unit so the variants compile in parallel.
+extern const SkinnyVariant kSkinnyPartBf16Nt1[];
+extern const int kSkinnyPartBf16Nt1Count;
+extern const SkinnyVariant kSkinnyPartBf16Nt2[];
+extern const int kSkinnyPartBf16Nt2Count;
+extern const SkinnyVariant kSkinnyPartF32[];
+extern const int kSkinnyPartF32Count;
+
+// (waves, spw) pairs compiled for every (nt, rb, f32w) combination.
+#define GDP_WAVES_SPW(X, NT, RB, F32W)                                                   \
+    X(NT, RB, 4, 2, F32W) X(NT, RB, 4, 4, F32W) X(NT, RB, 4, 8, F32W)                       \
+    X(NT, RB, 4, 16, F32W) X(NT, RB, 4, 32, F32W) X(NT, RB, 8, 2, F32W)                     \
+    X(NT, RB, 8, 4, F32W) X(NT, RB, 8, 8, F32W) X(NT, RB, 8, 16, F32W)                      \
+    X(NT, RB, 8, 32, F32W) X(NT, RB, 16, 2, F32W) X(NT, RB, 16, 4, F32W)                    \
+    X(NT, RB, 16, 8, F32W) X(NT, RB, 16, 16, F32W)
+
+}  // namespace gdp

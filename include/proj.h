@@ -1,0 +1,168 @@
+/*
+ * proj.h - C ABI of the MI355X decode-projection library.
+ *
+ * The library computes one bias-free linear layer per call,
+ *     out[i, n] = sum over k of x[i, k] * W[n, k]      (out = x @ W^T),
+ * for five fixed weight matrices (guide ch. 1 "The problem, the judge and the
+ * speed of light", §1.1, layer table):
+ *
+ *     layer      id  N x K         W      out
+ *     qkv_gate    0  2304 x 8192   BF16   BF16
+ *     o           1  8192 x 1024   BF16   BF16
+ *     pooler      2  4096 x 8192   BF16   BF16
+ *     unpooler    3  8192 x 4096   BF16   BF16  (m <= 8: only rows 0..1023)
+ *     router      4   256 x 8192   FP32   FP32
+ *
+ * x is always BF16, m x K row-major. Accumulation is FP32 (notebook note
+ * "Numerical formats and error": BF16 operands, FP32 accumulation, BF16
+ * output). The call contract follows guide ch. 1 §1.6: weights are handed
+ * over once to an untimed prepare step; the timed call is replayed inside a
+ * graph, so it never synchronizes and branches on shapes only.
+ *
+ * Pointers named "device" are HIP device pointers of the device that was
+ * current when the layer was prepared. Streams are hipStream_t passed as
+ * void * (NULL = the null stream). Every function returns PROJ_OK (0) or a
+ * negative proj_status; no function aborts the process.
+ *
+ * Threading: calls that touch one layer must not race each other. Launches
+ * of one layer that overlap on the GPU must not share the layer's split-K
+ * workspace: at most one proj_run per layer may be in flight at a time
+ * (stream order of a single stream satisfies this).
+ */
+#ifndef PROJ_H
+#define PROJ_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum proj_layer {
+    PROJ_QKV_GATE = 0,
+    PROJ_O = 1,
+    PROJ_POOLER = 2,
+    PROJ_UNPOOLER = 3,
+    PROJ_ROUTER = 4,
+    PROJ_NUM_LAYERS = 5
+};
+
+enum proj_status {
+    PROJ_OK = 0,
+    PROJ_ERR_LAYER = -1,        /* layer id not in 0..4 */
+    PROJ_ERR_M = -2,            /* m < 1, or m above PROJ_MAX_M */
+    PROJ_ERR_NULL = -3,         /* a required pointer is NULL */
+    PROJ_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
+    PROJ_ERR_NOT_PREPARED = -5, /* proj_run before proj_prepare for that layer */
+    PROJ_ERR_UNSUPPORTED = -6,  /* a requested kernel configuration is not built */
+    PROJ_ERR_HIP = -7,          /* a HIP runtime call failed (see proj_last_hip_error) */
+    PROJ_ERR_DEVICE = -8        /* current device differs from the one the layer was prepared on */
+};
+
+/* Largest token count a call accepts (sizes the split-K workspace). */
+#define PROJ_MAX_M 4096
+
+/*
+ * proj_prepare - repack a layer's weights once (guide ch. 1 §1.6: prepare runs
+ * once, untimed; the report's round-6 note and the notebook's packed-pooler
+ * notes describe the same lossless reordering of W into the kernel's read
+ * order).
+ *
+ * W: device pointer, N x K row-major contiguous, BF16 bit patterns (uint16)
+ *    for layers 0..3 and FP32 for the router. Read only during the call; the
+ *    caller keeps ownership and may free it on return.
+ * Effect: allocates library-owned device memory for the packed copy (same
+ *    byte count as W) and the layer's split-K workspace, runs the repack on
+ *    the null stream and synchronizes the device. Preparing a prepared layer
+ *    replaces its weights. The device current at this call becomes the
+ *    layer's device.
+ * Errors: PROJ_ERR_LAYER, PROJ_ERR_NULL, PROJ_ERR_ALIGN, PROJ_ERR_HIP.
+ */
+int proj_prepare(int layer, const void *W);
+
+/*
+ * proj_run - out = x @ W^T for `m` tokens, launch only (guide ch. 1 §1.1 for
+ * the operation, §1.6 for the graph-replay contract).
+ *
+ * x:   device, m x K row-major BF16 bits, 16-byte aligned.
+ * out: device, m x proj_out_cols(layer, m) row-major, BF16 bits (router:
+ *      FP32), 16-byte aligned. Fully overwritten.
+ * stream: hipStream_t (NULL = null stream).
+ * Effect: exactly one kernel launch on `stream`. No allocation, no
+ *    synchronization, no host read of device memory, no memset; the choice
+ *    of kernel depends on (layer, m) only. Safe to capture in a HIP graph and
+ *    replay with new contents of x. Split-K counters (if the chosen kernel
+ *    uses them) are reset on the GPU by the kernel itself.
+ * Errors (checked on the host before launching): PROJ_ERR_LAYER, PROJ_ERR_M,
+ *    PROJ_ERR_NULL, PROJ_ERR_ALIGN, PROJ_ERR_NOT_PREPARED, PROJ_ERR_DEVICE;
+ *    PROJ_ERR_HIP if the launch is rejected.
+ */
+int proj_run(int layer, const void *x, int m, void *out, void *stream);
+
+/*
+ * proj_out_cols - columns of out: N, except 1024 for the unpooler at m <= 8
+ * (guide ch. 1 §1.1: at <= 8 tokens only this GPU's slice, the first 1024
+ * rows, is computed). Returns a negative proj_status for a bad layer or m.
+ */
+int proj_out_cols(int layer, int m);
+
+/*
+ * proj_layer_dims - the layer table: N, K and the element sizes of W and out
+ * in bytes (2 for BF16, 4 for FP32). Any output pointer may be NULL.
+ */
+int proj_layer_dims(int layer, int *N, int *K, int *w_elem_bytes, int *out_elem_bytes);
+
+/* proj_release - free a layer's packed weights and workspace; idempotent. */
+int proj_release(int layer);
+
+/* proj_strerror - static text for a proj_status value. */
+const char *proj_strerror(int status);
+
+/* proj_last_hip_error - the hipError_t behind the last PROJ_ERR_HIP. */
+int proj_last_hip_error(void);
+
+/*
+ * Kernel configurations (the m-keyed dispatch table and the tuner's view).
+ *
+ * A configuration names one compiled kernel variant plus its split:
+ *   kind      0 = skinny MFMA kernel (16-row blocks, waves split K in the
+ *               workgroup), 1 = tiled MFMA kernel (large m)
+ *   nt        token sub-tiles of 16 per workgroup
+ *   rb        16-row blocks per workgroup
+ *   waves     wavefronts per workgroup
+ *   spw       k-steps of 32 per wave (kind 0); k-steps per stage (kind 1)
+ *   ksplit    workgroups that split K for one tile (1 = no cross-workgroup
+ *             reduction; >1 = last-arriving workgroup sums the partials in
+ *             split order)
+ *   flags     bit 0 set: workgroup i keeps tile i. Clear (default): when the
+ *             grid is a multiple of 8, consecutive tiles are grouped on one
+ *             XCD (workgroups are dealt to the 8 XCDs round-robin).
+ * proj_plan fills the configuration proj_run would use; proj_run_config runs
+ * an explicit one and returns PROJ_ERR_UNSUPPORTED if it is not compiled or
+ * does not tile the layer.
+ */
+typedef struct {
+    int kind;
+    int nt;
+    int rb;
+    int waves;
+    int spw;
+    int ksplit;
+    int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping) */
+    int grid;      /* filled by proj_plan: workgroups launched */
+    int block;     /* filled by proj_plan: threads per workgroup */
+} proj_config;
+
+int proj_plan(int layer, int m, proj_config *cfg);
+int proj_run_config(int layer, const void *x, int m, void *out, void *stream,
+                    const proj_config *cfg);
+
+/* Number of compiled variants and the i-th one (ksplit = 1). */
+int proj_num_variants(void);
+int proj_variant(int i, int *is_f32w, proj_config *cfg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROJ_H */

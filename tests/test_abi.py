@@ -1,0 +1,102 @@
+"""The C-ABI library loads and exports what include/*.h declares (CPU only: no GPU calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gemv_decode_projections_amd import binding, layers
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in ("proj.h", "proj_bench.h"):
+        with open(os.path.join(ROOT, "include", h)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(proj_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from gemv_decode_projections_amd import build
+
+        build.build()
+    return binding._lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 15, names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+
+
+def test_layer_table_matches_python_side(lib):
+    for name in layers.LAYERS:
+        n, k, wb, ob = binding.proj_layer_dims(name)
+        assert (n, k, wb, ob) == layers.DIMS[name]
+        for m in (1, 8, 9, 256, 4096):
+            assert binding.proj_out_cols(name, m) == layers.n_eff(name, m)
+
+
+def test_host_side_errors_without_gpu(lib):
+    vp = ctypes.c_void_p
+    assert lib.proj_out_cols(5, 1) == -1
+    assert lib.proj_out_cols(-1, 1) == -1
+    assert lib.proj_out_cols(0, 0) == -2
+    assert lib.proj_out_cols(0, binding.PROJ_MAX_M + 1) == -2
+    assert lib.proj_run(7, vp(16), 1, vp(16), vp(0)) == -1
+    assert lib.proj_run(0, vp(16), 0, vp(16), vp(0)) == -2
+    assert lib.proj_run(0, vp(0), 1, vp(16), vp(0)) == -3
+    assert lib.proj_run(0, vp(8), 1, vp(16), vp(0)) == -4
+    assert lib.proj_run(0, vp(16), 1, vp(16), vp(0)) == -5       # not prepared
+    assert lib.proj_prepare(9, vp(16)) == -1
+    assert lib.proj_prepare(0, vp(0)) == -3
+    assert lib.proj_prepare(0, vp(4)) == -4
+    assert lib.proj_release(2) == 0 and lib.proj_release(2) == 0  # idempotent
+    assert lib.proj_release(11) == -1
+    for s in range(-8, 1):
+        assert binding.proj_strerror(s) != "unknown status"
+
+
+def test_dispatch_plans_tile_every_layer(lib):
+    # Every (layer, m) resolves to a compiled variant that tiles the layer exactly.
+    for name in layers.LAYERS:
+        n, k, _, _ = layers.DIMS[name]
+        for m in list(range(1, 41)) + [64, 100, 127, 128, 129, 130, 200, 256, 512, 1000, 4096]:
+            cfg = binding.proj_plan(name, m)
+            ne = layers.n_eff(name, m)
+            assert cfg.waves * cfg.spw * cfg.ksplit == k // 32
+            assert ne % (16 * cfg.rb) == 0
+            n_tt = -(-m // (16 * cfg.nt))
+            assert cfg.grid == ne // (16 * cfg.rb) * n_tt * cfg.ksplit
+            assert cfg.block == 64 * cfg.waves
+
+
+def test_variant_registry(lib):
+    nv = binding.proj_num_variants()
+    assert nv > 0
+    seen = set()
+    for i in range(nv):
+        f32, cfg = binding.proj_variant(i)
+        key = (f32, cfg.nt, cfg.rb, cfg.waves, cfg.spw)
+        assert key not in seen
+        seen.add(key)
+    with pytest.raises(binding.ProjError):
+        binding.proj_variant(nv)
+
+
+def test_run_config_rejects_untiled_configs(lib):
+    # Host-side rejection happens before any GPU work; the layer is unprepared
+    # here, so the first error reported is NOT_PREPARED for valid pointers.
+    cfg = binding.ProjConfig.make(nt=1, rb=1, waves=8, spw=3, ksplit=1)
+    rc = lib.proj_run_config(0, ctypes.c_void_p(16), 1, ctypes.c_void_p(16), ctypes.c_void_p(0),
+                             ctypes.byref(cfg))
+    assert rc == -5

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle.
+
+Bounds (guide ch. 1 "The problem, the judge and the speed of light", §1.5):
+global relative L2 <= 1e-2 (router 1e-4), probe rows <= 1e-3, no row above
+5x the bound, no NaN/Inf. Inputs are the seeded synthetic workloads of
+workload/ (shapes of §1.1, loads and awkward m of §1.2).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from workload import LAYERS, LOADS, AWKWARD_M, SHAPES, make_weight, make_x, bf16_bits_from_f32
+from workload.generate import f32_from_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts only with -m gpu
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gemv_decode_projections_amd import binding  # noqa: E402
+from tests.gpu_util import (Prepared, run_layer, compare, sample_rows, say, to_device_x,  # noqa: E402
+                            to_device_weight, out_to_f64)
+
+_state = {"seed": None, "prep": None}
+
+
+def prepared(seed):
+    if _state["seed"] != seed:
+        say("preparing all layers, weight seed", seed)
+        _state["prep"] = Prepared(seed)
+        _state["seed"] = seed
+    return _state["prep"]
+
+
+def _dirty():
+    _state["seed"] = None
+
+
+def test_mfma_lane_layout():
+    rng = np.random.default_rng(0)
+    A = rng.integers(-4, 5, size=(16, 32)).astype(np.float32)
+    B = rng.integers(-4, 5, size=(32, 16)).astype(np.float32)
+    Ad = to_device_x(bf16_bits_from_f32(A))
+    Bd = to_device_x(bf16_bits_from_f32(B))
+    C = torch.full((16, 16), float("nan"), dtype=torch.float32, device="cuda")
+    binding.proj_bench_mfma_layout(Ad, Bd, C)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), A @ B)
+
+
+@pytest.mark.parametrize("variant", ["normal", "probe"])
+def test_o_projection_m1(variant):
+    p = prepared(0)
+    xs = make_x("o", 1, seed=100, probe_variant=(variant == "probe"))
+    say("o m=1", variant)
+    got = run_layer("o", xs.bits)
+    r = compare("o", got, p.w["o"], xs)
+    assert r.ok, r
+    if variant == "probe":
+        (row, k, e), = xs.probes
+        col = f32_from_bf16_bits(p.w["o"][:, k]).astype(np.float64) * 2.0 ** e
+        assert np.array_equal(got[row], col)   # an exact scaled weight column
+
+
+@pytest.mark.parametrize("outliers", [False, True], ids=["normal", "outlier"])
+@pytest.mark.parametrize("layer", LAYERS)
+@pytest.mark.parametrize("load", list(LOADS))
+def test_loads(load, layer, outliers):
+    p = prepared(0)
+    m = LOADS[load]
+    xs = make_x(layer, m, seed=200, outliers=outliers)
+    say("load", load, layer, "m=%d" % m, "outliers" if outliers else "normal")
+    got = run_layer(layer, xs.bits)
+    r = compare(layer, got, p.w[layer], xs)
+    assert r.ok, r
+
+
+@pytest.mark.parametrize("outliers", [False, True], ids=["normal", "outlier"])
+@pytest.mark.parametrize("layer", LAYERS)
+@pytest.mark.parametrize("m", AWKWARD_M)
+@pytest.mark.parametrize("wseed", [0, 1])
+def test_awkward_m(wseed, m, layer, outliers):
+    p = prepared(wseed)
+    xs = make_x(layer, m, seed=300 + wseed, outliers=outliers)
+    say("awkward", layer, "m=%d" % m, "wseed=%d" % wseed, "outliers" if outliers else "normal")
+    got = run_layer(layer, xs.bits)
+    rows = sample_rows(xs, m) if m >= 100 else None
+    r = compare(layer, got, p.w[layer], xs, rows)
+    assert r.ok, r
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 6, 11, 13, 15, 17, 20, 24, 31, 40, 48, 64, 100])
+def test_more_token_counts(m):
+    p = prepared(0)
+    for layer in LAYERS:
+        xs = make_x(layer, m, seed=400, outliers=(m % 2 == 1))
+        say("extra m", layer, "m=%d" % m)
+        got = run_layer(layer, xs.bits)
+        r = compare(layer, got, p.w[layer], xs)
+        assert r.ok, (layer, r)
+
+
+def _variant_cases():
+    cases = []
+    for i in range(binding.proj_num_variants()):
+        f32, cfg = binding.proj_variant(i)
+        cands = ["router"] if f32 else ["o", "unpooler", "qkv_gate"]
+        for layer in cands:
+            ks = SHAPES[layer][1] // 32
+            if ks % (cfg.waves * cfg.spw) == 0:
+                split = ks // (cfg.waves * cfg.spw)
+                cases.append((layer, cfg.nt, cfg.rb, cfg.waves, cfg.spw, split))
+                break
+    return cases
+
+
+@pytest.mark.parametrize("case", _variant_cases(), ids=lambda c: "%s-nt%d-rb%d-w%d-s%d-k%d" % c)
+def test_every_compiled_variant(case):
+    layer, nt, rb, waves, spw, split = case
+    p = prepared(0)
+    for m in sorted({1, 16 * nt - 3, 16 * nt + 5}):
+        if layer == "unpooler" and m > 8:
+            continue
+        cfg = binding.ProjConfig.make(nt=nt, rb=rb, waves=waves, spw=spw, ksplit=split)
+        xs = make_x(layer, m, seed=500 + m, outliers=True)
+        say("variant", case, "m=%d" % m)
+        got = run_layer(layer, xs.bits, cfg=cfg)
+        r = compare(layer, got, p.w[layer], xs)
+        assert r.ok, (case, m, r)
+
+
+@pytest.mark.parametrize("layer", LAYERS)
+def test_output_rows_beyond_m_untouched(layer):
+    prepared(0)
+    m = 5
+    xs = make_x(layer, m, seed=600)
+    ncol = binding.proj_out_cols(layer, m)
+    big = torch.full((m + 3, ncol), float("nan"), dtype=binding.out_dtype(layer), device="cuda")
+    say("tail", layer)
+    binding.proj_run(layer, to_device_x(xs.bits), m, big)
+    torch.cuda.synchronize()
+    g = out_to_f64(big)
+    assert np.all(np.isfinite(g[:m])) and np.all(np.isnan(g[m:]))
+
+
+@pytest.mark.parametrize("layer", LAYERS)
+@pytest.mark.parametrize("m", [1, 8, 16, 32, 33])
+def test_graph_replay_fresh_inputs(layer, m):
+    """Captured once, replayed with new x each time: split-K counters must reset
+    on the GPU and nothing may be cached from an earlier x (guide ch. 1 §1.6)."""
+    p = prepared(0)
+    k = SHAPES[layer][1]
+    x_static = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
+    out = binding.new_out(layer, m)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.proj_run(layer, x_static, m, out, s)   # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.proj_run(layer, x_static, m, out, s)
+    say("graph", layer, "m=%d" % m)
+    prev_bits = None
+    for rep in range(6):
+        xs = make_x(layer, m, seed=700 + rep, outliers=(rep % 2 == 1))
+        x_static.copy_(to_device_x(xs.bits))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_to_f64(out)
+        r = compare(layer, got, p.w[layer], xs)
+        assert r.ok, (rep, r)
+        if rep == 0:
+            prev_bits = out.clone()
+    # Same x again: bit-identical result (fixed reduction order).
+    xs = make_x(layer, m, seed=700)
+    x_static.copy_(to_device_x(xs.bits))
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32),
+                       prev_bits.view(torch.int16) if out.dtype == torch.bfloat16 else prev_bits.view(torch.int32))
+
+
+def test_bf16_output_rounding_is_nearest_even():
+    """Exact FP32 sums that fall halfway between two BF16 values round to the even one."""
+    _dirty()
+    n, k = SHAPES["o"]
+    j = np.arange(n) % 128
+    a = (1.0 + j * 2.0 ** -7).astype(np.float32)                 # exact in BF16
+    b = np.choose(np.arange(n) % 4, [1.0, -1.0, 3.0, 0.5]).astype(np.float32)
+    w = np.zeros((n, k), dtype=np.float32)
+    w[:, 0] = a
+    w[:, 1] = b
+    wb = bf16_bits_from_f32(w)
+    binding.proj_prepare("o", to_device_weight("o", wb))
+    x = np.zeros((1, k), dtype=np.float32)
+    x[0, 0] = 1.0
+    x[0, 1] = 2.0 ** -8
+    got = run_layer("o", bf16_bits_from_f32(x))
+    exact = (a.astype(np.float64) + b.astype(np.float64) * 2.0 ** -8)
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)  # sums exact in FP32
+    want = f32_from_bf16_bits(bf16_bits_from_f32(exact.astype(np.float32))).astype(np.float64)
+    assert np.array_equal(got[0], want)
+    _dirty()
+
+
+def test_router_keeps_fp32_weight_bits():
+    """Router weights that BF16 cannot hold must still reach the sum exactly: a
+    probe row returns the FP32 weight column bit for bit."""
+    p = prepared(0)
+    xs = make_x("router", 1, seed=800, probe_variant=True)
+    got = run_layer("router", xs.bits)
+    (row, kk, e), = xs.probes
+    want = p.w["router"][:, kk].astype(np.float64) * 2.0 ** e
+    assert np.array_equal(got[row], want)
