@@ -22,6 +22,7 @@ SOURCES = [
     "skinny_bf16_nt1.hip",
     "skinny_bf16_nt2.hip",
     "skinny_f32.hip",
+    "tiled_variants.hip",
 ]
 
 ARCH = os.environ.get("GDP_OFFLOAD_ARCH", "gfx950")
@@ -36,11 +37,18 @@ COMMON = [
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source extra flags. Tiled kernels keep MFMA accumulators in VGPRs: with
+# AGPR accumulators the register allocator rotates them across the unrolled
+# k-steps and copies them back every loop trip (measured slower for the
+# skinny kernels, so only here).
+EXTRA = {
+    "tiled_variants.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src, verbose):
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -8,6 +8,7 @@
 #include "../../include/proj_bench.h"
 #include "repack.h"
 #include "skinny.h"
+#include "tiled.h"
 #include "variants.h"
 
 namespace gdp {
@@ -32,13 +33,14 @@ constexpr LayerInfo kLayers[PROJ_NUM_LAYERS] = {
 constexpr int kSliceMaxM = 8;        // unpooler computes rows 0..1023 at m <= 8
 constexpr int kSliceRows = 1024;
 
-constexpr size_t kWsBytes = 8u << 20;        // split-K partials per layer
+constexpr size_t kWsBytes = 32u << 20;       // split-K partials per layer
 constexpr size_t kCounters = 1u << 16;       // split-K arrival counters per layer
 
 struct LayerState {
     void *wp = nullptr;
     f32x4 *ws = nullptr;
     uint32_t *counters = nullptr;
+    uint16_t *zrow = nullptr;     // K zero BF16 values: activation rows past m
     int device = -1;
     bool prepared = false;
 };
@@ -74,10 +76,19 @@ const SkinnyVariant *find_variant(int nt, int rb, int waves, int spw, int f32w)
     return nullptr;
 }
 
-int total_variants()
+const TiledVariant *find_tiled(int bmb, int bnb, int waves, int depth, int f32w)
 {
-    return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count;
+    for (int i = 0; i < kTiledVariantCount; ++i) {
+        const TiledVariant &v = kTiledVariants[i];
+        if (v.bmb == bmb && v.bnb == bnb && v.wr * v.wc == waves && v.depth == depth && v.f32w == f32w)
+            return &v;
+    }
+    return nullptr;
 }
+
+int skinny_variants() { return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count; }
+
+int total_variants() { return skinny_variants() + kTiledVariantCount; }
 
 const SkinnyVariant *variant_at(int i)
 {
@@ -94,10 +105,12 @@ const SkinnyVariant *variant_at(int i)
     return nullptr;
 }
 
-// Resolved launch of one configuration.
+// Resolved launch of one configuration (one of the two argument blocks is used).
 struct Launch {
-    const SkinnyVariant *v;
-    SkinnyArgs args;
+    const void *fn;
+    int kind;
+    SkinnyArgs sargs;
+    TiledArgs targs;
     int grid;
     int block;
 };
@@ -106,45 +119,90 @@ struct Launch {
 int resolve(int layer, int m, const proj_config &c, Launch &L)
 {
     const LayerInfo &li = kLayers[layer];
-    if (c.kind != 0)
-        return PROJ_ERR_UNSUPPORTED;
     const int f32w = li.w_bytes == 4 ? 1 : 0;
-    const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w);
-    if (!v || c.ksplit < 1)
-        return PROJ_ERR_UNSUPPORTED;
     const int KS = li.K / kStepK;
-    if (c.waves * c.spw * c.ksplit != KS)
-        return PROJ_ERR_UNSUPPORTED;
     const int ne = n_eff_of(layer, m);
-    if (ne % (kRowsPerBlock * c.rb) != 0)
-        return PROJ_ERR_UNSUPPORTED;
-    const int n_rt = ne / (kRowsPerBlock * c.rb);
-    const int n_tt = (m + 16 * c.nt - 1) / (16 * c.nt);
-    const long long grid = (long long)n_rt * n_tt * c.ksplit;
-    if (grid < 1 || grid > 0x7fffffffLL)
-        return PROJ_ERR_UNSUPPORTED;
-    if (c.ksplit > 1) {
-        const long long elems = (long long)c.rb * c.nt * kWave;
-        if ((long long)n_rt * n_tt * c.ksplit * elems * (long long)sizeof(f32x4) > (long long)kWsBytes)
-            return PROJ_ERR_UNSUPPORTED;
-        if ((long long)n_rt * n_tt > (long long)kCounters)
-            return PROJ_ERR_UNSUPPORTED;
-    }
     const LayerState &st = g_layers[layer];
-    L.v = v;
-    L.grid = (int)grid;
-    L.block = c.waves * kWave;
-    L.args.wp = st.wp;
-    L.args.ws = st.ws;
-    L.args.counters = st.counters;
-    L.args.m = m;
-    L.args.K = li.K;
-    L.args.n_eff = ne;
-    L.args.n_rt = n_rt;
-    L.args.n_tt = n_tt;
-    L.args.ksplit = c.ksplit;
-    L.args.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
-    return PROJ_OK;
+    if (c.ksplit < 1)
+        return PROJ_ERR_UNSUPPORTED;
+    if (c.kind == 0) {
+        const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w);
+        if (!v)
+            return PROJ_ERR_UNSUPPORTED;
+        if (c.waves * c.spw * c.ksplit != KS)
+            return PROJ_ERR_UNSUPPORTED;
+        if (ne % (kRowsPerBlock * c.rb) != 0)
+            return PROJ_ERR_UNSUPPORTED;
+        const int n_rt = ne / (kRowsPerBlock * c.rb);
+        const int n_tt = (m + 16 * c.nt - 1) / (16 * c.nt);
+        const long long grid = (long long)n_rt * n_tt * c.ksplit;
+        if (grid < 1 || grid > 0x7fffffffLL)
+            return PROJ_ERR_UNSUPPORTED;
+        if (c.ksplit > 1) {
+            const long long elems = (long long)c.rb * c.nt * kWave;
+            if ((long long)n_rt * n_tt * c.ksplit * elems * (long long)sizeof(f32x4) > (long long)kWsBytes)
+                return PROJ_ERR_UNSUPPORTED;
+            if ((long long)n_rt * n_tt > (long long)kCounters)
+                return PROJ_ERR_UNSUPPORTED;
+        }
+        L.fn = v->fn;
+        L.kind = 0;
+        L.grid = (int)grid;
+        L.block = c.waves * kWave;
+        SkinnyArgs &A = L.sargs;
+        A.wp = st.wp;
+        A.ws = st.ws;
+        A.counters = st.counters;
+        A.m = m;
+        A.K = li.K;
+        A.n_eff = ne;
+        A.n_rt = n_rt;
+        A.n_tt = n_tt;
+        A.ksplit = c.ksplit;
+        A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
+        return PROJ_OK;
+    }
+    if (c.kind == 1) {
+        // rb = 16-row blocks per tile, nt = 16-token blocks per tile,
+        // spw = prefetch depth in k-steps
+        const TiledVariant *v = find_tiled(c.rb, c.nt, c.waves, c.spw, f32w);
+        if (!v)
+            return PROJ_ERR_UNSUPPORTED;
+        if (KS % (c.spw * c.ksplit) != 0)       // k-steps per workgroup: a multiple of the depth
+            return PROJ_ERR_UNSUPPORTED;
+        if (ne % (kRowsPerBlock * c.rb) != 0)
+            return PROJ_ERR_UNSUPPORTED;
+        const int n_rt = ne / (kRowsPerBlock * c.rb);
+        const int n_tt = (m + 16 * c.nt - 1) / (16 * c.nt);
+        const long long grid = (long long)n_rt * n_tt * c.ksplit;
+        if (grid < 1 || grid > 0x7fffffffLL)
+            return PROJ_ERR_UNSUPPORTED;
+        if (c.ksplit > 1) {
+            const long long tile_bytes = (long long)c.rb * c.nt * kWave * 16;
+            if ((long long)n_rt * n_tt * c.ksplit * tile_bytes > (long long)kWsBytes)
+                return PROJ_ERR_UNSUPPORTED;
+            if ((long long)n_rt * n_tt > (long long)kCounters)
+                return PROJ_ERR_UNSUPPORTED;
+        }
+        L.fn = v->fn;
+        L.kind = 1;
+        L.grid = (int)grid;
+        L.block = c.waves * kWave;
+        TiledArgs &A = L.targs;
+        A.wp = st.wp;
+        A.zrow = st.zrow;
+        A.ws = reinterpret_cast<float *>(st.ws);
+        A.counters = st.counters;
+        A.m = m;
+        A.K = li.K;
+        A.n_eff = ne;
+        A.n_rt = n_rt;
+        A.n_tt = n_tt;
+        A.ksplit = c.ksplit;
+        A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
+        return PROJ_OK;
+    }
+    return PROJ_ERR_UNSUPPORTED;
 }
 
 // The m-keyed dispatch table. Shapes only: (layer, m) -> configuration.
@@ -180,13 +238,33 @@ proj_config plan_default(int layer, int m)
         c.ksplit = e.ksplit;
         return c;
     }
-    // Larger m: token tiles of 32 across the grid.
-    const int KS = kLayers[layer].K / kStepK;
-    c.nt = 2;
-    c.rb = 1;
-    c.waves = 8;
-    c.spw = KS / 8;
-    c.ksplit = 1;
+    // Larger m: tiled kernel, picked per layer from measured sweeps. Buckets:
+    // m <= 64, m <= 128, larger. Entries: rows blocks (rb), token blocks (nt),
+    // waves, prefetch depth, K split. Past 256 tokens the split halves until
+    // the grid is at most ~3 workgroups per compute unit and the partials fit
+    // the workspace.
+    struct TEntry {
+        int rb, nt, waves, depth, ksplit;
+    };
+    static const TEntry ttable[PROJ_NUM_LAYERS][3] = {
+        /* qkv_gate */ {{4, 4, 4, 4, 4}, {8, 4, 4, 8, 4}, {8, 4, 4, 8, 2}},
+        /* o        */ {{4, 4, 4, 4, 1}, {4, 4, 4, 4, 1}, {8, 4, 4, 8, 1}},
+        /* pooler   */ {{4, 4, 4, 8, 4}, {8, 4, 4, 8, 4}, {8, 4, 4, 8, 2}},
+        /* unpooler */ {{4, 4, 4, 4, 2}, {8, 4, 4, 8, 2}, {8, 4, 4, 8, 1}},
+        /* router   */ {{4, 4, 4, 4, 16}, {4, 4, 4, 4, 8}, {4, 4, 4, 4, 8}},
+    };
+    const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : 2)];
+    const int ne = n_eff_of(layer, m);
+    c.kind = 1;
+    c.rb = e.rb;
+    c.nt = e.nt;
+    c.waves = e.waves;
+    c.spw = e.depth;
+    const long tiles = (long)(ne / (16 * c.rb)) * ((m + 16 * c.nt - 1) / (16 * c.nt));
+    int ks = e.ksplit;
+    while (ks > 1 && (tiles * ks > 768 || tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes))
+        ks /= 2;
+    c.ksplit = ks;
     return c;
 }
 
@@ -217,15 +295,17 @@ int check_run_args(int layer, const void *x, int m, void *out)
 int launch(const Launch &L, const void *x, void *out, hipStream_t stream, hipEvent_t ev_start = nullptr,
            hipEvent_t ev_stop = nullptr)
 {
-    SkinnyArgs args = L.args;
-    args.x = static_cast<const uint16_t *>(x);
-    args.out = out;
-    void *params[] = {&args};
+    SkinnyArgs sargs = L.sargs;
+    TiledArgs targs = L.targs;
+    sargs.x = targs.x = static_cast<const uint16_t *>(x);
+    sargs.out = targs.out = out;
+    void *params[1];
+    params[0] = L.kind == 0 ? static_cast<void *>(&sargs) : static_cast<void *>(&targs);
     hipError_t e;
     if (ev_start || ev_stop)
-        e = hipExtLaunchKernel(L.v->fn, dim3(L.grid), dim3(L.block), params, 0, stream, ev_start, ev_stop, 0);
+        e = hipExtLaunchKernel(L.fn, dim3(L.grid), dim3(L.block), params, 0, stream, ev_start, ev_stop, 0);
     else
-        e = hipLaunchKernel(L.v->fn, dim3(L.grid), dim3(L.block), params, 0, stream);
+        e = hipLaunchKernel(L.fn, dim3(L.grid), dim3(L.block), params, 0, stream);
     if (e != hipSuccess)
         return hip_fail(e);
     return PROJ_OK;
@@ -239,6 +319,8 @@ void free_layer(LayerState &st)
         (void)hipFree(st.ws);
     if (st.counters)
         (void)hipFree(st.counters);
+    if (st.zrow)
+        (void)hipFree(st.zrow);
     st = LayerState{};
 }
 
@@ -270,7 +352,9 @@ int proj_prepare(int layer, const void *W)
     if ((e = hipMalloc(&ns.wp, wbytes)) != hipSuccess ||
         (e = hipMalloc(reinterpret_cast<void **>(&ns.ws), kWsBytes)) != hipSuccess ||
         (e = hipMalloc(reinterpret_cast<void **>(&ns.counters), kCounters * sizeof(uint32_t))) != hipSuccess ||
-        (e = hipMemset(ns.counters, 0, kCounters * sizeof(uint32_t))) != hipSuccess) {
+        (e = hipMemset(ns.counters, 0, kCounters * sizeof(uint32_t))) != hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void **>(&ns.zrow), (size_t)li.K * 2)) != hipSuccess ||
+        (e = hipMemset(ns.zrow, 0, (size_t)li.K * 2)) != hipSuccess) {
         free_layer(ns);
         return hip_fail(e);
     }
@@ -403,6 +487,23 @@ int proj_num_variants(void) { return total_variants(); }
 
 int proj_variant(int i, int *is_f32w, proj_config *cfg)
 {
+    if (i >= skinny_variants() && i < total_variants()) {
+        const TiledVariant &t = kTiledVariants[i - skinny_variants()];
+        if (is_f32w)
+            *is_f32w = t.f32w;
+        if (cfg) {
+            proj_config c{};
+            c.kind = 1;
+            c.nt = t.bnb;
+            c.rb = t.bmb;
+            c.waves = t.wr * t.wc;
+            c.spw = t.depth;
+            c.ksplit = 1;
+            c.block = c.waves * kWave;
+            *cfg = c;
+        }
+        return PROJ_OK;
+    }
     const SkinnyVariant *v = variant_at(i);
     if (!v)
         return PROJ_ERR_UNSUPPORTED;

@@ -16,7 +16,8 @@
 //   * A workgroup owns RB row blocks, NT*16 tokens and a K range; its WAVES
 //     waves split that K range into contiguous runs of SPW k-steps.
 //   * Activations are the B operand, loaded straight from x (L2-resident
-//     after the first touch); lanes of tokens >= m load nothing.
+//     after the first touch) with quad-contiguous reads and permuted across
+//     lanes into the MFMA layout; lanes of tokens >= m are zeroed.
 //   * Loads are double-buffered in registers in stages of U k-steps; each
 //     wave starts its run at a rotated k-step (spreads activation requests
 //     over L2 channels).
@@ -78,26 +79,31 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
     const int rb0 = rt * RB;
 
     const u32x4 *wbase = reinterpret_cast<const u32x4 *>(a.wp);
-    const int kk = 8 * (lane / 16);
     // Each wave walks its k-steps starting at a rotated position, so waves of
     // one workgroup and neighbouring workgroups on an XCD do not all request
     // the same activation lines (and L2 channel) at the same moment.
     const int rot = (2 * (wave + WAVES * (int)(blockIdx.x / 8))) & (SPW - 1);
     static_assert((SPW & (SPW - 1)) == 0, "SPW must be a power of two");
 
-    // Token of this lane's B column in each sub-tile.
-    int tok[NT];
+    // Activations. The MFMA wants lane l to hold token l%16, k = 8*(l/16)+0..7,
+    // which as a load would make every lane quad touch four rows (measured
+    // ~3x slower than quad-contiguous reads from L2). So lane s loads token
+    // s/4, k = 8*(s%4)+0..7 -- each quad one contiguous 64-byte row segment --
+    // and the fragment is moved to the MFMA layout with a lane permutation
+    // (destination lane l takes source lane 4*(l%16) + l/16).
     bool tok_ok[NT];
     const uint16_t *xrow[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        tok[t] = tt * 16 * NT + t * 16 + (lane % 16);
-        tok_ok[t] = tok[t] < a.m;
-        // Lanes past the last token read row m-1 (always valid) and zero it
-        // afterwards: a select instead of a branch keeps the load pipeline free
-        // of control-flow joins, which would force a wait for every load.
-        xrow[t] = a.x + (size_t)(tok_ok[t] ? tok[t] : a.m - 1) * a.K + kk;
+        const int tok = tt * 16 * NT + t * 16 + (lane % 16);       // this lane's MFMA column
+        tok_ok[t] = tok < a.m;
+        const int tok_ld = tt * 16 * NT + t * 16 + lane / 4;       // the row this lane loads
+        // Rows past the last token read row m-1 (always valid); their lanes are
+        // zeroed after the permutation. A select instead of a branch keeps the
+        // load pipeline free of control-flow joins, which force a full wait.
+        xrow[t] = a.x + (size_t)(tok_ld < a.m ? tok_ld : a.m - 1) * a.K + 8 * (lane % 4);
     }
+    const int perm_src = 4 * (lane % 16) + lane / 16;             // bpermute source lane
 
     f32x4 acc[RB][NT];
 #pragma unroll
@@ -132,9 +138,13 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                if (!tok_ok[t])
-                    xb[buf][u][t] = u32x4{0u, 0u, 0u, 0u};
+            for (int t = 0; t < NT; ++t) {
+                u32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_src * 4, (int)xb[buf][u][t][i]);
+                xb[buf][u][t] = tok_ok[t] ? v : u32x4{0u, 0u, 0u, 0u};
+            }
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 if constexpr (F32W) {

@@ -14,6 +14,18 @@ struct SkinnyVariant {
     const void *fn;   // __global__ void (SkinnyArgs)
 };
 
+// Tiled (large-m) kernel variants: BMB x BNB blocks of 16 per workgroup, WR x WC waves
+// (WR = waves, WC = 1: waves split the rows).
+struct TiledVariant {
+    int bmb;
+    int bnb;
+    int wr;
+    int wc;
+    int depth;        // prefetch distance in k-steps
+    int f32w;
+    const void *fn;   // __global__ void (TiledArgs)
+};
+
 // Each part is defined in its own translation unit so the variants compile in parallel.
 extern const SkinnyVariant kSkinnyPartBf16Nt1[];
 extern const int kSkinnyPartBf16Nt1Count;
@@ -21,6 +33,8 @@ extern const SkinnyVariant kSkinnyPartBf16Nt2[];
 extern const int kSkinnyPartBf16Nt2Count;
 extern const SkinnyVariant kSkinnyPartF32[];
 extern const int kSkinnyPartF32Count;
+extern const TiledVariant kTiledVariants[];
+extern const int kTiledVariantCount;
 
 // (waves, spw) pairs compiled for every (nt, rb, f32w) combination.
 #define GDP_WAVES_SPW(X, NT, RB, F32W)                                                   \

@@ -126,11 +126,13 @@ int proj_last_hip_error(void);
  *
  * A configuration names one compiled kernel variant plus its split:
  *   kind      0 = skinny MFMA kernel (16-row blocks, waves split K in the
- *               workgroup), 1 = tiled MFMA kernel (large m)
+ *               workgroup), 1 = tiled MFMA kernel (large m; weight and
+ *               activation tiles staged in LDS)
  *   nt        token sub-tiles of 16 per workgroup
  *   rb        16-row blocks per workgroup
  *   waves     wavefronts per workgroup
- *   spw       k-steps of 32 per wave (kind 0); k-steps per stage (kind 1)
+ *   spw       k-steps of 32 per wave (kind 0); prefetch distance in k-steps
+ *             (kind 1; the k-steps of one workgroup must be a multiple of it)
  *   ksplit    workgroups that split K for one tile (1 = no cross-workgroup
  *             reduction; >1 = last-arriving workgroup sums the partials in
  *             split order)

@@ -73,7 +73,11 @@ def test_dispatch_plans_tile_every_layer(lib):
         for m in list(range(1, 41)) + [64, 100, 127, 128, 129, 130, 200, 256, 512, 1000, 4096]:
             cfg = binding.proj_plan(name, m)
             ne = layers.n_eff(name, m)
-            assert cfg.waves * cfg.spw * cfg.ksplit == k // 32
+            if cfg.kind == 0:
+                assert cfg.waves * cfg.spw * cfg.ksplit == k // 32
+            else:
+                assert cfg.kind == 1 and (k // 32) % (cfg.spw * cfg.ksplit) == 0
+                assert m > 32
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
             assert cfg.grid == ne // (16 * cfg.rb) * n_tt * cfg.ksplit
@@ -86,7 +90,7 @@ def test_variant_registry(lib):
     seen = set()
     for i in range(nv):
         f32, cfg = binding.proj_variant(i)
-        key = (f32, cfg.nt, cfg.rb, cfg.waves, cfg.spw)
+        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw)
         assert key not in seen
         seen.add(key)
     with pytest.raises(binding.ProjError):

@@ -23,6 +23,7 @@ from tests.gpu_util import (Prepared, run_layer, compare, sample_rows, say, to_d
                             to_device_weight, out_to_f64)
 
 _state = {"seed": None, "prep": None}
+WS_BYTES = 32 << 20  # split-K workspace per layer (proj_prepare)
 
 
 def prepared(seed):
@@ -102,32 +103,61 @@ def test_more_token_counts(m):
 
 
 def _variant_cases():
+    """Every compiled variant on a layer it tiles: (layer, kind, nt, rb, waves, spw, ksplit, flags)."""
     cases = []
     for i in range(binding.proj_num_variants()):
         f32, cfg = binding.proj_variant(i)
         cands = ["router"] if f32 else ["o", "unpooler", "qkv_gate"]
         for layer in cands:
-            ks = SHAPES[layer][1] // 32
-            if ks % (cfg.waves * cfg.spw) == 0:
-                split = ks // (cfg.waves * cfg.spw)
-                cases.append((layer, cfg.nt, cfg.rb, cfg.waves, cfg.spw, split))
+            n, k = SHAPES[layer]
+            ks = k // 32
+            if cfg.kind == 0:
+                if ks % (cfg.waves * cfg.spw) == 0:
+                    split = ks // (cfg.waves * cfg.spw)
+                    cases.append((layer, 0, cfg.nt, cfg.rb, cfg.waves, cfg.spw, split, 0))
+                    break
+            elif n % (16 * cfg.rb) == 0:
+                cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 1, 0))
+                cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 2, 0))
+                cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 2, 1))  # split groups across XCDs
                 break
     return cases
 
 
-@pytest.mark.parametrize("case", _variant_cases(), ids=lambda c: "%s-nt%d-rb%d-w%d-s%d-k%d" % c)
+@pytest.mark.parametrize("case", _variant_cases(), ids=lambda c: "%s-kind%d-nt%d-rb%d-w%d-s%d-k%d-f%d" % c)
 def test_every_compiled_variant(case):
-    layer, nt, rb, waves, spw, split = case
+    layer, kind, nt, rb, waves, spw, split, flags = case
     p = prepared(0)
-    for m in sorted({1, 16 * nt - 3, 16 * nt + 5}):
-        if layer == "unpooler" and m > 8:
+    ms = [1, 16 * nt - 3, 16 * nt + 5] if kind == 0 else [33, 16 * nt + 5, 3 * 16 * nt - 7]
+    for m in sorted(set(ms)):
+        if layer == "unpooler" and m > 8 and kind == 0:
             continue
-        cfg = binding.ProjConfig.make(nt=nt, rb=rb, waves=waves, spw=spw, ksplit=split)
+        if kind == 1 and split > 1:
+            n_tiles = (SHAPES[layer][0] // (16 * rb)) * -(-m // (16 * nt))
+            if n_tiles * split * rb * nt * 1024 > WS_BYTES:
+                continue  # the library rejects it: split-K workspace is 32 MB per layer
+        cfg = binding.ProjConfig.make(kind=kind, nt=nt, rb=rb, waves=waves, spw=spw, ksplit=split, flags=flags)
         xs = make_x(layer, m, seed=500 + m, outliers=True)
         say("variant", case, "m=%d" % m)
         got = run_layer(layer, xs.bits, cfg=cfg)
         r = compare(layer, got, p.w[layer], xs)
         assert r.ok, (case, m, r)
+
+
+@pytest.mark.parametrize("layer,m", [("router", 1), ("router", 32), ("unpooler", 8)])
+def test_split_k_across_xcds(layer, m):
+    """Split-K groups spread over different XCDs (no workgroup grouping) still reduce correctly."""
+    p = prepared(0)
+    cfg = binding.proj_plan(layer, m)
+    if cfg.ksplit == 1:
+        ks = SHAPES[layer][1] // 32
+        cfg = binding.ProjConfig.make(nt=cfg.nt, rb=cfg.rb, waves=4, spw=ks // 16, ksplit=4)
+    cfg.flags = 1
+    for rep in range(3):
+        xs = make_x(layer, m, seed=900 + rep, outliers=True)
+        got = run_layer(layer, xs.bits, cfg=cfg)
+        r = compare(layer, got, p.w[layer], xs)
+        assert r.ok, (rep, r)
 
 
 @pytest.mark.parametrize("layer", LAYERS)
