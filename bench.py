@@ -171,6 +171,23 @@ def traffic_for(layer, m):
     return int(round(k["fetch_bytes"] + k["write_bytes"]))
 
 
+def kernel_name(cfg, f32w):
+    """Template name of the kernel a configuration launches (as profilers print it)."""
+    f = "true" if f32w else "false"
+    if cfg.kind == 0:
+        return "skinny_kernel<%d, %d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.waves, cfg.spw, f)
+    if cfg.kind == 1:
+        return "tiled_kernel<%d, %d, %d, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.waves, cfg.spw, f)
+    return "rowdot_kernel<%d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.spw, f)
+
+
+PROJ_KERNELS = ("skinny_kernel", "tiled_kernel", "rowdot_kernel")
+
+
+def _is_proj_kernel(name):
+    return any(k in name for k in PROJ_KERNELS)
+
+
 def _read_csv(path):
     import csv
 
@@ -183,7 +200,7 @@ def summarize_trace(trace_csv, steps, warmup):
     from workload import LAYERS
 
     rows = sorted(_read_csv(trace_csv), key=lambda r: int(r["Start_Timestamp"]))
-    sk = [r for r in rows if "skinny_kernel" in r["Kernel_Name"]]
+    sk = [r for r in rows if _is_proj_kernel(r["Kernel_Name"])]
     timed = sk[warmup * len(LAYERS):(warmup + steps) * len(LAYERS)]
     out = {}
     for i, layer in enumerate(LAYERS):
@@ -206,7 +223,7 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes=64 << 20):
     for path, cname, key in ((fetch_csv, "FETCH_SIZE", "fetch"), (write_csv, "WRITE_SIZE", "write")):
         rows = sorted((r for r in _read_csv(path) if r["Counter_Name"] == cname),
                       key=lambda r: int(r["Dispatch_Id"]))
-        sk = [r for r in rows if "skinny_kernel" in r["Kernel_Name"]]
+        sk = [r for r in rows if _is_proj_kernel(r["Kernel_Name"])]
         cp = [float(r["Counter_Value"]) for r in rows if "copy_kernel" in r["Kernel_Name"]]
         scale = copy_bytes / (statistics.median(cp) * 1024.0)
         res[key + "_scale"] = round(scale, 4)
@@ -325,8 +342,7 @@ def main():
     dom_bytes = rf.bytes_of(dom, 1)
     achieved = dom_bytes / dom_avg / 1e3  # GB/s
     cfg = B.proj_plan(dom, 1)
-    kname = "skinny_kernel<%d, %d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.waves, cfg.spw,
-                                                    "true" if dom == "router" else "false")
+    kname = kernel_name(cfg, dom == "router")
     roof = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dom, 1),

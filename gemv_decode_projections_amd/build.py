@@ -23,6 +23,7 @@ SOURCES = [
     "skinny_bf16_nt2.hip",
     "skinny_f32.hip",
     "tiled_variants.hip",
+    "rowdot_variants.hip",
 ]
 
 ARCH = os.environ.get("GDP_OFFLOAD_ARCH", "gfx950")

@@ -7,6 +7,7 @@
 #include "../../include/proj.h"
 #include "../../include/proj_bench.h"
 #include "repack.h"
+#include "rowdot.h"
 #include "skinny.h"
 #include "tiled.h"
 #include "variants.h"
@@ -33,6 +34,11 @@ constexpr LayerInfo kLayers[PROJ_NUM_LAYERS] = {
 constexpr int kSliceMaxM = 8;        // unpooler computes rows 0..1023 at m <= 8
 constexpr int kSliceRows = 1024;
 
+// Rows kept in row-major order for the row-dot kernel: the whole router and
+// the unpooler's slice (the other layers have enough 16-row blocks to fill
+// the chip with the MFMA kernels).
+constexpr int kRowMajorRows[PROJ_NUM_LAYERS] = {0, 0, 0, kSliceRows, 256};
+
 constexpr size_t kWsBytes = 32u << 20;       // split-K partials per layer
 constexpr size_t kCounters = 1u << 16;       // split-K arrival counters per layer
 
@@ -41,6 +47,8 @@ struct LayerState {
     f32x4 *ws = nullptr;
     uint32_t *counters = nullptr;
     uint16_t *zrow = nullptr;     // K zero BF16 values: activation rows past m
+    void *wrow = nullptr;         // row-major copy of the first wrow_rows rows (row-dot kernel)
+    int wrow_rows = 0;
     int device = -1;
     bool prepared = false;
 };
@@ -86,9 +94,19 @@ const TiledVariant *find_tiled(int bmb, int bnb, int waves, int depth, int f32w)
     return nullptr;
 }
 
+const RowVariant *find_row(int mcap, int r, int kit, int f32w)
+{
+    for (int i = 0; i < kRowVariantCount; ++i) {
+        const RowVariant &v = kRowVariants[i];
+        if (v.mcap == mcap && v.r == r && v.kit == kit && v.f32w == f32w)
+            return &v;
+    }
+    return nullptr;
+}
+
 int skinny_variants() { return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count; }
 
-int total_variants() { return skinny_variants() + kTiledVariantCount; }
+int total_variants() { return skinny_variants() + kTiledVariantCount + kRowVariantCount; }
 
 const SkinnyVariant *variant_at(int i)
 {
@@ -111,6 +129,7 @@ struct Launch {
     int kind;
     SkinnyArgs sargs;
     TiledArgs targs;
+    RowArgs rargs;
     int grid;
     int block;
 };
@@ -202,6 +221,26 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
         return PROJ_OK;
     }
+    if (c.kind == 2) {
+        // nt = token capacity, rb = rows per workgroup, spw = 2048-wide k chunks per row
+        const RowVariant *v = find_row(c.nt, c.rb, c.spw, f32w);
+        if (!v || c.waves != kRowWaves || c.ksplit != 1)
+            return PROJ_ERR_UNSUPPORTED;
+        if (m > c.nt || ne > kRowMajorRows[layer] || ne % c.rb != 0)
+            return PROJ_ERR_UNSUPPORTED;
+        if (li.K != c.spw * kRowThreads * 8)
+            return PROJ_ERR_UNSUPPORTED;
+        L.fn = v->fn;
+        L.kind = 2;
+        L.grid = ne / c.rb;
+        L.block = kRowThreads;
+        RowArgs &A = L.rargs;
+        A.w = st.wrow;
+        A.m = m;
+        A.K = li.K;
+        A.n_eff = ne;
+        return PROJ_OK;
+    }
     return PROJ_ERR_UNSUPPORTED;
 }
 
@@ -217,17 +256,30 @@ proj_config plan_default(int layer, int m)
     // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32.
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {2, 1, 8, 32, 1}},
+        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {2, 2, 4, 32, 2}},
         /* o         512 row blocks,  32 k-steps */
         {{1, 2, 4, 8, 1}, {1, 2, 4, 8, 1}, {2, 2, 4, 8, 1}},
         /* pooler    256 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {2, 1, 8, 32, 1}},
+        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {2, 2, 4, 32, 2}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
-        {{1, 1, 8, 16, 1}, {1, 2, 8, 16, 1}, {2, 2, 4, 32, 1}},
+        {{1, 1, 8, 16, 1}, {1, 1, 4, 32, 1}, {2, 2, 4, 32, 1}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
-        {{1, 1, 4, 16, 4}, {1, 1, 4, 16, 4}, {2, 1, 4, 16, 4}},
+        {{1, 1, 8, 4, 8}, {1, 1, 16, 2, 8}, {2, 1, 16, 2, 8}},
     };
     proj_config c{};
+    // Few tokens on the router (m <= 8) and the unpooler slice (m <= 4):
+    // whole rows per workgroup (row-dot kernel), token capacity rounded up to
+    // a power of two. Past 4 tokens the unpooler slice re-reads too much
+    // activation data per row and the skinny kernel is faster.
+    if ((layer == PROJ_ROUTER && m <= 8) || (layer == PROJ_UNPOOLER && m <= 4)) {
+        c.kind = 2;
+        c.nt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
+        c.rb = layer == PROJ_ROUTER ? 1 : (m <= 2 ? 2 : 4);
+        c.waves = kRowWaves;
+        c.spw = kLayers[layer].K / (kRowThreads * 8);
+        c.ksplit = 1;
+        return c;
+    }
     c.kind = 0;
     if (m <= 32) {
         const Entry &e = table[layer][m <= 8 ? 0 : (m <= 16 ? 1 : 2)];
@@ -297,10 +349,13 @@ int launch(const Launch &L, const void *x, void *out, hipStream_t stream, hipEve
 {
     SkinnyArgs sargs = L.sargs;
     TiledArgs targs = L.targs;
-    sargs.x = targs.x = static_cast<const uint16_t *>(x);
-    sargs.out = targs.out = out;
+    RowArgs rargs = L.rargs;
+    sargs.x = targs.x = rargs.x = static_cast<const uint16_t *>(x);
+    sargs.out = targs.out = rargs.out = out;
     void *params[1];
-    params[0] = L.kind == 0 ? static_cast<void *>(&sargs) : static_cast<void *>(&targs);
+    params[0] = L.kind == 0   ? static_cast<void *>(&sargs)
+                : L.kind == 1 ? static_cast<void *>(&targs)
+                              : static_cast<void *>(&rargs);
     hipError_t e;
     if (ev_start || ev_stop)
         e = hipExtLaunchKernel(L.fn, dim3(L.grid), dim3(L.block), params, 0, stream, ev_start, ev_stop, 0);
@@ -321,6 +376,8 @@ void free_layer(LayerState &st)
         (void)hipFree(st.counters);
     if (st.zrow)
         (void)hipFree(st.zrow);
+    if (st.wrow)
+        (void)hipFree(st.wrow);
     st = LayerState{};
 }
 
@@ -357,6 +414,15 @@ int proj_prepare(int layer, const void *W)
         (e = hipMemset(ns.zrow, 0, (size_t)li.K * 2)) != hipSuccess) {
         free_layer(ns);
         return hip_fail(e);
+    }
+    if (kRowMajorRows[layer] > 0) {
+        const size_t rbytes = (size_t)kRowMajorRows[layer] * li.K * li.w_bytes;
+        if ((e = hipMalloc(&ns.wrow, rbytes)) != hipSuccess ||
+            (e = hipMemcpy(ns.wrow, W, rbytes, hipMemcpyDeviceToDevice)) != hipSuccess) {
+            free_layer(ns);
+            return hip_fail(e);
+        }
+        ns.wrow_rows = kRowMajorRows[layer];
     }
     const int threads = 256;
     const int blocks = 4096;
@@ -487,6 +553,23 @@ int proj_num_variants(void) { return total_variants(); }
 
 int proj_variant(int i, int *is_f32w, proj_config *cfg)
 {
+    if (i >= skinny_variants() + kTiledVariantCount && i < total_variants()) {
+        const RowVariant &r = kRowVariants[i - skinny_variants() - kTiledVariantCount];
+        if (is_f32w)
+            *is_f32w = r.f32w;
+        if (cfg) {
+            proj_config c{};
+            c.kind = 2;
+            c.nt = r.mcap;
+            c.rb = r.r;
+            c.waves = kRowWaves;
+            c.spw = r.kit;
+            c.ksplit = 1;
+            c.block = kRowThreads;
+            *cfg = c;
+        }
+        return PROJ_OK;
+    }
     if (i >= skinny_variants() && i < total_variants()) {
         const TiledVariant &t = kTiledVariants[i - skinny_variants()];
         if (is_f32w)

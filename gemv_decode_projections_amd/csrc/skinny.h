@@ -246,20 +246,19 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
     // multi-XCD part; no L2 write-back or invalidate is needed. Each wave
     // waits until its partial stores are complete before the barrier, so the
     // arrival that thread 0 counts afterwards covers the whole workgroup.
-    float *wsf = reinterpret_cast<float *>(wsp);
-    auto publish = [&](int e, f32x4 v) {
-        float *d = wsf + ((size_t)ks * ELEMS + e) * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __hip_atomic_store(d + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    if constexpr (WAVES > 1) {
-        for (int e = threadIdx.x; e < ELEMS; e += WAVES * kWave)
-            publish(e, wave_sum(e));
-    } else {
-#pragma unroll
-        for (int j = 0; j < TILES; ++j)
-            publish(j * kWave + lane, acc[j / NT][j % NT]);
+    // Values move as 8-byte words (an f32x4 is two words, low element first).
+    // The last workgroup gathers WAVES splits per round, one per wave, with
+    // all of a wave's loads in flight at once, and sums them through LDS.
+    constexpr int NTHR = WAVES * kWave;
+    constexpr int EPT = (ELEMS + NTHR - 1) / NTHR;  // output elements per thread
+    uint64_t *wsw = reinterpret_cast<uint64_t *>(wsp);
+    for (int e = threadIdx.x; e < ELEMS; e += NTHR) {
+        // Whole-vector bit cast: a bit cast of one vector element reads element 0.
+        const u32x4 u = __builtin_bit_cast(u32x4, wave_sum(e));
+        uint64_t *d = wsw + ((size_t)ks * ELEMS + e) * 2;
+        __hip_atomic_store(d, (uint64_t)u.x | ((uint64_t)u.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d + 1, (uint64_t)u.z | ((uint64_t)u.w << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -271,15 +270,43 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
     __syncthreads();
     if (!s_last)
         return;
-    for (int e = threadIdx.x; e < ELEMS; e += WAVES * kWave) {
-        f32x4 v{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < a.ksplit; ++s) {
-            const float *src = wsf + ((size_t)s * ELEMS + e) * 4;
+    f32x4 v[EPT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < EPT; ++i)
+        v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.ksplit; s0 += WAVES) {
+        // Waves past the last split re-read it (valid memory, never summed).
+        const int sp = min(s0 + wave, a.ksplit - 1);
+        const uint64_t *src = wsw + (size_t)sp * ELEMS * 2;
+        uint64_t wd[TILES][2];
+#pragma unroll
+        for (int j = 0; j < TILES; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wd[j][h] = __hip_atomic_load(src + (j * kWave + lane) * 2 + h, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();                             // earlier readers of red are done
+#pragma unroll
+        for (int j = 0; j < TILES; ++j) {
+            const u32x4 u = {(uint32_t)wd[j][0], (uint32_t)(wd[j][0] >> 32), (uint32_t)wd[j][1],
+                             (uint32_t)(wd[j][1] >> 32)};
+            red[wave][j][lane] = __builtin_bit_cast(f32x4, u);
         }
-        store_out(e, v);
+        __syncthreads();
+        const int nw = min(WAVES, a.ksplit - s0);
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = threadIdx.x + i * NTHR;
+            if (e < ELEMS)
+                for (int w = 0; w < nw; ++w)
+                    v[i] += red[w][e / kWave][e % kWave];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * NTHR;
+        if (e < ELEMS)
+            store_out(e, v[i]);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -26,6 +26,15 @@ struct TiledVariant {
     const void *fn;   // __global__ void (TiledArgs)
 };
 
+// Row-dot (few tokens, few rows) kernel variants.
+struct RowVariant {
+    int mcap;         // largest token count
+    int r;            // rows per workgroup
+    int kit;          // 2048-wide k chunks per row
+    int f32w;
+    const void *fn;   // __global__ void (RowArgs)
+};
+
 // Each part is defined in its own translation unit so the variants compile in parallel.
 extern const SkinnyVariant kSkinnyPartBf16Nt1[];
 extern const int kSkinnyPartBf16Nt1Count;
@@ -35,6 +44,8 @@ extern const SkinnyVariant kSkinnyPartF32[];
 extern const int kSkinnyPartF32Count;
 extern const TiledVariant kTiledVariants[];
 extern const int kTiledVariantCount;
+extern const RowVariant kRowVariants[];
+extern const int kRowVariantCount;
 
 // (waves, spw) pairs compiled for every (nt, rb, f32w) combination.
 #define GDP_WAVES_SPW(X, NT, RB, F32W)                                                   \

@@ -73,7 +73,10 @@ enum proj_status {
  *    caller keeps ownership and may free it on return.
  * Effect: allocates library-owned device memory for the packed copy (same
  *    byte count as W) and the layer's split-K workspace, runs the repack on
- *    the null stream and synchronizes the device. Preparing a prepared layer
+ *    the null stream and synchronizes the device. For the router (all 256
+ *    rows) and the unpooler (its first 1024 rows) it also keeps a plain
+ *    row-major copy of those rows for the row-dot kernel used at m <= 8
+ *    (8 MB each). Preparing a prepared layer
  *    replaces its weights. The device current at this call becomes the
  *    layer's device.
  * Errors: PROJ_ERR_LAYER, PROJ_ERR_NULL, PROJ_ERR_ALIGN, PROJ_ERR_HIP.
@@ -127,12 +130,17 @@ int proj_last_hip_error(void);
  * A configuration names one compiled kernel variant plus its split:
  *   kind      0 = skinny MFMA kernel (16-row blocks, waves split K in the
  *               workgroup), 1 = tiled MFMA kernel (large m; weight and
- *               activation tiles staged in LDS)
- *   nt        token sub-tiles of 16 per workgroup
- *   rb        16-row blocks per workgroup
- *   waves     wavefronts per workgroup
+ *               activation tiles staged in LDS), 2 = row-dot kernel (m <= 8,
+ *               router and the unpooler's 1024-row slice only: whole rows per
+ *               workgroup from a row-major weight copy, FP32 multiply-adds)
+ *   nt        token sub-tiles of 16 per workgroup (kinds 0, 1); largest token
+ *             count of the variant (kind 2)
+ *   rb        16-row blocks per workgroup (kinds 0, 1); rows per workgroup
+ *             (kind 2)
+ *   waves     wavefronts per workgroup (4 for kind 2)
  *   spw       k-steps of 32 per wave (kind 0); prefetch distance in k-steps
- *             (kind 1; the k-steps of one workgroup must be a multiple of it)
+ *             (kind 1; the k-steps of one workgroup must be a multiple of it);
+ *             k chunks of 2048 per row (kind 2: K = 2048 * spw)
  *   ksplit    workgroups that split K for one tile (1 = no cross-workgroup
  *             reduction; >1 = last-arriving workgroup sums the partials in
  *             split order)

@@ -73,6 +73,13 @@ def test_dispatch_plans_tile_every_layer(lib):
         for m in list(range(1, 41)) + [64, 100, 127, 128, 129, 130, 200, 256, 512, 1000, 4096]:
             cfg = binding.proj_plan(name, m)
             ne = layers.n_eff(name, m)
+            assert cfg.block == 64 * cfg.waves
+            if cfg.kind == 2:
+                # whole rows per workgroup: router and the unpooler slice at m <= 8
+                assert name in ("router", "unpooler") and m <= cfg.nt <= 8 and cfg.ksplit == 1
+                assert cfg.spw * 2048 == k
+                assert ne % cfg.rb == 0 and cfg.grid == ne // cfg.rb
+                continue
             if cfg.kind == 0:
                 assert cfg.waves * cfg.spw * cfg.ksplit == k // 32
             else:
@@ -81,7 +88,6 @@ def test_dispatch_plans_tile_every_layer(lib):
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
             assert cfg.grid == ne // (16 * cfg.rb) * n_tt * cfg.ksplit
-            assert cfg.block == 64 * cfg.waves
 
 
 def test_variant_registry(lib):

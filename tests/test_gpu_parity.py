@@ -107,6 +107,9 @@ def _variant_cases():
     cases = []
     for i in range(binding.proj_num_variants()):
         f32, cfg = binding.proj_variant(i)
+        if cfg.kind == 2:
+            cases.append(("router" if f32 else "unpooler", 2, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 1, 0))
+            continue
         cands = ["router"] if f32 else ["o", "unpooler", "qkv_gate"]
         for layer in cands:
             n, k = SHAPES[layer]
@@ -128,7 +131,12 @@ def _variant_cases():
 def test_every_compiled_variant(case):
     layer, kind, nt, rb, waves, spw, split, flags = case
     p = prepared(0)
-    ms = [1, 16 * nt - 3, 16 * nt + 5] if kind == 0 else [33, 16 * nt + 5, 3 * 16 * nt - 7]
+    if kind == 0:
+        ms = [1, 16 * nt - 3, 16 * nt + 5]
+    elif kind == 1:
+        ms = [33, 16 * nt + 5, 3 * 16 * nt - 7]
+    else:
+        ms = [1, nt // 2 + 1, nt]      # row-dot: up to its token capacity
     for m in sorted(set(ms)):
         if layer == "unpooler" and m > 8 and kind == 0:
             continue
@@ -149,9 +157,9 @@ def test_split_k_across_xcds(layer, m):
     """Split-K groups spread over different XCDs (no workgroup grouping) still reduce correctly."""
     p = prepared(0)
     cfg = binding.proj_plan(layer, m)
-    if cfg.ksplit == 1:
+    if cfg.kind != 0 or cfg.ksplit == 1:
         ks = SHAPES[layer][1] // 32
-        cfg = binding.ProjConfig.make(nt=cfg.nt, rb=cfg.rb, waves=4, spw=ks // 16, ksplit=4)
+        cfg = binding.ProjConfig.make(nt=1, rb=1, waves=4, spw=ks // 16, ksplit=4)
     cfg.flags = 1
     for rep in range(3):
         xs = make_x(layer, m, seed=900 + rep, outliers=True)
