@@ -88,7 +88,7 @@ const TiledVariant *find_tiled(int bmb, int bnb, int waves, int depth, int f32w)
 {
     for (int i = 0; i < kTiledVariantCount; ++i) {
         const TiledVariant &v = kTiledVariants[i];
-        if (v.bmb == bmb && v.bnb == bnb && v.wr * v.wc == waves && v.depth == depth && v.f32w == f32w)
+        if (v.bmb == bmb && v.bnb == bnb && v.wr * v.kg == waves && v.depth == depth && v.f32w == f32w)
             return &v;
     }
     return nullptr;
@@ -183,11 +183,11 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
     }
     if (c.kind == 1) {
         // rb = 16-row blocks per tile, nt = 16-token blocks per tile,
-        // spw = prefetch depth in k-steps
+        // spw = prefetch depth in super-steps (kg k-steps each)
         const TiledVariant *v = find_tiled(c.rb, c.nt, c.waves, c.spw, f32w);
         if (!v)
             return PROJ_ERR_UNSUPPORTED;
-        if (KS % (c.spw * c.ksplit) != 0)       // k-steps per workgroup: a multiple of the depth
+        if (KS % (c.spw * c.ksplit * v->kg) != 0)   // k-steps per workgroup: a multiple of kg * depth
             return PROJ_ERR_UNSUPPORTED;
         if (ne % (kRowsPerBlock * c.rb) != 0)
             return PROJ_ERR_UNSUPPORTED;
@@ -291,19 +291,19 @@ proj_config plan_default(int layer, int m)
         return c;
     }
     // Larger m: tiled kernel, picked per layer from measured sweeps. Buckets:
-    // m <= 64, m <= 128, larger. Entries: rows blocks (rb), token blocks (nt),
-    // waves, prefetch depth, K split. Past 256 tokens the split halves until
+    // m <= 64, m <= 128, larger. Entries: row blocks (rb), token blocks (nt),
+    // waves, weight prefetch depth in k-steps, K split. Past 256 tokens the split halves until
     // the grid is at most ~3 workgroups per compute unit and the partials fit
     // the workspace.
     struct TEntry {
         int rb, nt, waves, depth, ksplit;
     };
     static const TEntry ttable[PROJ_NUM_LAYERS][3] = {
-        /* qkv_gate */ {{4, 4, 4, 4, 4}, {8, 4, 4, 8, 4}, {8, 4, 4, 8, 2}},
-        /* o        */ {{4, 4, 4, 4, 1}, {4, 4, 4, 4, 1}, {8, 4, 4, 8, 1}},
-        /* pooler   */ {{4, 4, 4, 8, 4}, {8, 4, 4, 8, 4}, {8, 4, 4, 8, 2}},
-        /* unpooler */ {{4, 4, 4, 4, 2}, {8, 4, 4, 8, 2}, {8, 4, 4, 8, 1}},
-        /* router   */ {{4, 4, 4, 4, 16}, {4, 4, 4, 4, 8}, {4, 4, 4, 4, 8}},
+        /* qkv_gate */ {{4, 4, 4, 4, 4}, {8, 4, 4, 16, 4}, {8, 4, 4, 16, 2}},
+        /* o        */ {{4, 4, 4, 4, 1}, {4, 4, 4, 4, 1}, {8, 4, 4, 4, 1}},
+        /* pooler   */ {{4, 4, 4, 8, 4}, {8, 4, 4, 16, 4}, {8, 4, 4, 16, 2}},
+        /* unpooler */ {{4, 4, 4, 4, 2}, {4, 4, 4, 4, 1}, {8, 4, 4, 16, 1}},
+        /* router   */ {{4, 4, 4, 4, 16}, {4, 4, 4, 4, 16}, {4, 4, 4, 4, 8}},
     };
     const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : 2)];
     const int ne = n_eff_of(layer, m);
@@ -579,7 +579,7 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
             c.kind = 1;
             c.nt = t.bnb;
             c.rb = t.bmb;
-            c.waves = t.wr * t.wc;
+            c.waves = t.wr * t.kg;
             c.spw = t.depth;
             c.ksplit = 1;
             c.block = c.waves * kWave;

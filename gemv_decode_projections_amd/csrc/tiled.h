@@ -17,13 +17,15 @@
 //   * Weights (the HBM stream) go straight into registers, each wave reading
 //     its own 1 KB fragments (fragment-major packing, repack.h) D k-steps
 //     ahead of use.
-//   * Activations (L2-resident) are loaded cooperatively, D k-steps ahead,
-//     with quad-contiguous reads (each lane quad reads one token's 64-byte row
-//     segment, the four k-groups rotated per token), then written to a 4-slot
-//     LDS ring two k-steps ahead. The rotation makes both the 1 KB contiguous
-//     LDS writes and the MFMA-layout reads (lane l: token l%16, k =
-//     8*(l/16)+0..7) free of bank conflicts. Each k-step's B fragments are read
-//     from LDS during the previous k-step's MFMAs. One barrier per k-step.
+//   * Activations (L2-resident) are staged through a 4-slot LDS ring in
+//     super-steps of S k-steps: consecutive lanes read one token's S*64
+//     contiguous bytes, two super-steps ahead, and write them to the
+//     positions the MFMA reads (lane l: token l%16, k = 8*(l/16)+0..7),
+//     rotated per token and skewed per k-step so that both the writes and the
+//     fragment reads are free of bank conflicts. Each k-step's B fragments are
+//     read from LDS during the previous k-step's MFMAs. One barrier per
+//     super-step: with one barrier per k-step the barriers alone cost about a
+//     quarter of the kernel (measured by removing them).
 //   * v_mfma_f32_16x16x32_bf16 with FP32 accumulation; FP32 router weights are
 //     split exactly into three BF16 parts in registers (common.h).
 //   * K may be split over KSPLIT workgroups per tile; the split index varies
@@ -55,17 +57,23 @@ struct TiledArgs {
     int xcd_remap;
 };
 
-template <int RBW, int BNB, int WAVES, int D, bool F32W>
+template <int RBW, int BNB, int WAVES, int S, int D, bool F32W>
 __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
 {
     constexpr int NTHR = WAVES * kWave;
     constexpr int AW = F32W ? 2 : 1;                  // 1 KB units per weight fragment
     constexpr int BMB = WAVES * RBW;                  // row blocks per tile
-    static_assert(D >= 2 && (D & (D - 1)) == 0, "prefetch distance: power of two");
-    static_assert((BNB * kWave) % NTHR == 0, "activation fragments must split over threads");
-    constexpr int XPT = BNB * kWave / NTHR;           // activation units per thread per k-step
+    constexpr int PAD = S > 1 ? 4 : 0;                // units between k-step regions (bank skew)
+    constexpr int REG = BNB * kWave + PAD;            // LDS units per k-step region
+    constexpr int UNITS = S * BNB * kWave;            // 16-byte activation units per super-step
+    constexpr int CPT = 4 * S;                        // 16-byte chunks per token per super-step
+    static_assert(D >= S && D % S == 0 && (D & (D - 1)) == 0, "prefetch distance: power of two, whole super-steps");
+    static_assert(S == 1 || S == 2 || S == 4, "k-steps per super-step");
+    static_assert((D / S) % 2 == 0, "an even number of super-steps per unrolled pass (register ring of 2)");
+    static_assert(UNITS % NTHR == 0, "activation units must split over threads");
+    constexpr int XPT = UNITS / NTHR;                 // activation units per thread per super-step
 
-    __shared__ u32x4 xl[4][BNB * kWave];
+    __shared__ u32x4 xl[4][S * REG];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -84,33 +92,40 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
 
     const int KS = a.K / kStepK;
     const int steps = KS / a.ksplit;                  // k-steps of this workgroup (multiple of D)
+    const int nss = steps / S;                        // super-steps
     const int step0 = ks * steps;
     const int tok0 = tt * BNB * 16;
-    const int rbw0 = rt * BMB + wave * RBW;          // first row block of this wave
+    const int rbw0 = rt * BMB + wave * RBW;           // first row block of this wave
 
     const u32x4 *wbase = reinterpret_cast<const u32x4 *>(a.wp);
 
-    // Activation load plan for this thread (XPT units per k-step). Rows past
-    // the last token read a zero row instead of being masked afterwards: a
-    // select on loaded data gets hoisted next to the loads and forces waits.
+    // Activation load plan (XPT units per thread per super-step). Unit u reads
+    // 16-byte chunk c = u % CPT of token u / CPT: consecutive lanes read one
+    // token's S*64 contiguous bytes. Chunk c is k-step c/4, k-group c%4 of
+    // the super-step; it lands in LDS at the MFMA-read position of that
+    // k-group, rotated per token so that the fragment reads (lane l: token
+    // l%16, k-group l/16) hit distinct banks; k-step regions are skewed by PAD
+    // units so that the writes of one token's chunks do too. Rows past the
+    // last token read a zero row instead of being masked afterwards: a select
+    // on loaded data gets hoisted next to the loads and forces waits.
     const uint16_t *xsrc[XPT];
     int xdst[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
         const int u = i * NTHR + tid;
-        const int blk = u / kWave;
-        const int s = u % kWave;
-        const int q = s / 4;                          // token within the 16-token block
-        const int g = ((s % 4) - q / 4) & 3;          // rotated k-group
-        const int tok = tok0 + blk * 16 + q;
-        xsrc[i] = (tok < a.m ? a.x + (size_t)tok * a.K : a.zrow) + 8 * g;
-        xdst[i] = u;                                  // LDS unit (fragment blk, slot s)
+        const int c = u % CPT;
+        const int qt = u / CPT;                       // token within the tile
+        const int blk = qt / 16, q = qt % 16;
+        const int sub = c / 4, g = c % 4;
+        const int tok = tok0 + qt;
+        xsrc[i] = (tok < a.m ? a.x + (size_t)tok * a.K : a.zrow) + 8 * c;
+        xdst[i] = sub * REG + blk * kWave + 4 * q + ((g + q / 4) & 3);
     }
-    // LDS slot that holds (token l%16, k-group l/16) of a fragment for this lane.
+    // LDS unit that holds (token l%16, k-group l/16) of a fragment for this lane.
     const int bslot = 4 * (lane % 16) + (((lane / 16) + (lane % 16) / 4) & 3);
 
     u32x4 wr[D][RBW][AW];
-    u32x4 xr[D][XPT];
+    u32x4 xr[2][XPT];
     u32x4 br[2][BNB];
     f32x4 acc[RBW][BNB];
 #pragma unroll
@@ -119,7 +134,7 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
         for (int t = 0; t < BNB; ++t)
             acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto load_w = [&](int slot, int j) {
+    auto load_w = [&](int slot, int j) {              // k-step j of this workgroup
         const int st = step0 + (j < steps ? j : steps - 1);
 #pragma unroll
         for (int r = 0; r < RBW; ++r) {
@@ -129,8 +144,8 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
                 wr[slot][r][h] = f[h * kWave];
         }
     };
-    auto load_x = [&](int slot, int j) {
-        const int st = step0 + (j < steps ? j : steps - 1);
+    auto load_x = [&](int slot, int J) {              // super-step J
+        const int st = step0 + (J < nss ? J : nss - 1) * S;
 #pragma unroll
         for (int i = 0; i < XPT; ++i)
             xr[slot][i] = *reinterpret_cast<const u32x4 *>(xsrc[i] + (size_t)st * kStepK);
@@ -140,10 +155,10 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
         for (int i = 0; i < XPT; ++i)
             xl[buf][xdst[i]] = xr[slot][i];
     };
-    auto read_b = [&](int reg, int buf) {
+    auto read_b = [&](int reg, int buf, int sub) {
 #pragma unroll
         for (int t = 0; t < BNB; ++t)
-            br[reg][t] = xl[buf][t * kWave + bslot];
+            br[reg][t] = xl[buf][sub * REG + t * kWave + bslot];
     };
     auto compute = [&](int slot, int reg) {
 #pragma unroll
@@ -165,47 +180,67 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
         }
     };
 
-    // Pipeline (4 LDS slots, D register slots, two B-fragment register sets):
-    //   iteration j reads k-step j+1's fragments from LDS into br[(j+1)%2],
-    //   multiplies k-step j (wr[j%D], br[j%2]), writes k-step j+2's
-    //   activations from xr[(j+2)%D] to LDS slot (j+2)%4, refills wr[j%D] with
-    //   k-step j+D and xr[(j+2)%D] with k-step j+D+2, then one barrier.
-    // The LDS reads for the next k-step overlap this k-step's MFMAs; the
-    // barrier publishes slot (j+2)%4 for iteration j+1 and retires the reads of
-    // the slot that iteration j+2 overwrites (last read at iteration j-3).
-    // The prologue leaves the loads in flight in the order the loop does.
+    // Pipeline. Weights: register ring of D k-steps, k-step j+D loaded while
+    // k-step j is multiplied. Activations: super-step J+2 waits in registers
+    // (loaded two iterations earlier) and is written to LDS slot (J+2)%4 at
+    // iteration J; super-step J+4 is loaded in its place. Within iteration J,
+    // each k-step's B fragments are read from LDS during the previous
+    // k-step's MFMAs (across the super-step boundary too: slot (J+1)%4 was
+    // published by the barrier of iteration J-1). One barrier per super-step
+    // publishes slot (J+2)%4 and retires the reads of the slot iteration J+1
+    // overwrites (last read during iteration J-2 and the prefetch at the end of
+    // iteration J-3). The prologue leaves the loads in flight in the order the
+    // loop does.
     load_x(0, 0);
     load_x(1, 1);
     store_x(0, 0);
     store_x(1, 1);
+    load_x(0, 2);
+    load_x(1, 3);
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
+    for (int j = 0; j < D; ++j)
         load_w(j, j);
-        load_x((j + 2) % D, j + 2);
-    }
     __syncthreads();
-    read_b(0, 0);
+    read_b(0, 0, 0);
 
     for (int j0 = 0; j0 < steps; j0 += D) {
 #pragma unroll
         for (int jj = 0; jj < D; ++jj) {
             const int j = j0 + jj;
-            read_b((jj + 1) & 1, (jj + 1) & 3);
+            const int J = j / S;                      // super-step of k-step j
+            const int sub = jj % S;
+            // k-step j+1: same super-step, or the first of the next one.
+            if (sub + 1 < S)
+                read_b((jj + 1) & 1, J & 3, sub + 1);
+            else
+                read_b((jj + 1) & 1, (J + 1) & 3, 0);
             compute(jj, jj & 1);
-            store_x((jj + 2) % D, (jj + 2) & 3);
             load_w(jj, j + D);
-            load_x((jj + 2) % D, j + D + 2);
-            __syncthreads();
+            if (sub == S - 1) {
+                const int xs = (jj / S) & 1;          // == J & 1: j0 / S is even
+                store_x(xs, (J + 2) & 3);
+                load_x(xs, J + 4);
+                __syncthreads();
+            }
         }
     }
 
-    // Epilogue. Accumulator (r, t) covers rows (rbw0 + r)*16 + 4*(lane/16) + 0..3
-    // and token tok0 + t*16 + lane%16.
-    auto store_out = [&](int r, int t, f32x4 v) {
+    f32x4 fin[RBW][BNB];
+#pragma unroll
+    for (int r = 0; r < RBW; ++r)
+#pragma unroll
+        for (int t = 0; t < BNB; ++t)
+            fin[r][t] = acc[r][t];
+    constexpr int RBH = RBW;
+    const int rbf = rbw0;                             // first row block of this wave
+
+    // Epilogue. fin (h, t) covers rows (rbf + h)*16 + 4*(lane/16) + 0..3 and
+    // token tok0 + t*16 + lane%16.
+    auto store_out = [&](int h, int t, f32x4 v) {
         const int tk = tok0 + t * 16 + (lane % 16);
         if (tk >= a.m)
             return;
-        const int row = (rbw0 + r) * kRowsPerBlock + 4 * (lane / 16);
+        const int row = (rbf + h) * kRowsPerBlock + 4 * (lane / 16);
         if constexpr (F32W) {
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + (size_t)tk * a.n_eff + row) = v;
         } else {
@@ -218,33 +253,38 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
 
     if (a.ksplit == 1) {
 #pragma unroll
-        for (int r = 0; r < RBW; ++r)
+        for (int h = 0; h < RBH; ++h)
 #pragma unroll
             for (int t = 0; t < BNB; ++t)
-                store_out(r, t, acc[r][t]);
+                store_out(h, t, fin[h][t]);
         return;
     }
 
-    // Split-K: publish partials with agent-scope (write-through) stores, count
-    // arrivals, and let the last workgroup of the tile sum the partials in split
-    // order with agent-scope loads. Values move as 8-byte words, and the last
-    // workgroup issues every load of one split before using any of them.
+    // Split-K over workgroups: publish partials with agent-scope (write-through,
+    // visible to every XCD) 8-byte stores, wait until they are complete, count
+    // the arrival, and let the last workgroup of the tile gather the partials
+    // CH splits at a time with every load in flight, sum all splits in split
+    // order (deterministic), store the output and reset the counter for the
+    // next launch. (A variant where the last to arrive skips its own publish and
+    // polls a second counter for the others measured slower: the poll round
+    // trip costs more than the publish it saves.)
     constexpr int TILE_W = BMB * BNB * kWave * 2;     // 8-byte words per partial tile
-    constexpr int NW = RBW * BNB * 2;                 // words per thread
+    constexpr int NW = RBH * BNB * 2;                 // words per thread
+    constexpr int CH = 4;                             // splits gathered per round
     const int tile = rt * a.n_tt + tt;
     uint64_t *wsp = reinterpret_cast<uint64_t *>(a.ws) + (size_t)tile * a.ksplit * TILE_W;
-    auto word_of = [&](int r, int t, int h) { return (((wave * RBW + r) * BNB + t) * kWave + lane) * 2 + h; };
+    auto word_of = [&](int h, int t, int w) { return (((wave * RBH + h) * BNB + t) * kWave + lane) * 2 + w; };
     // Whole-vector bit casts only: a bit cast of a single vector element is
     // lowered by clang as a read of element 0.
 #pragma unroll
-    for (int r = 0; r < RBW; ++r)
+    for (int h = 0; h < RBH; ++h)
 #pragma unroll
         for (int t = 0; t < BNB; ++t) {
-            const u32x4 u = __builtin_bit_cast(u32x4, acc[r][t]);
+            const u32x4 u = __builtin_bit_cast(u32x4, fin[h][t]);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint64_t w = (uint64_t)u[2 * h] | ((uint64_t)u[2 * h + 1] << 32);
-                __hip_atomic_store(wsp + (size_t)ks * TILE_W + word_of(r, t, h), w, __ATOMIC_RELAXED,
+            for (int w = 0; w < 2; ++w) {
+                const uint64_t word = (uint64_t)u[2 * w] | ((uint64_t)u[2 * w + 1] << 32);
+                __hip_atomic_store(wsp + (size_t)ks * TILE_W + word_of(h, t, w), word, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -257,37 +297,53 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
     __syncthreads();
     if (!s_last)
         return;
+    f32x4 sum[RBH][BNB];
 #pragma unroll
-    for (int r = 0; r < RBW; ++r)
+    for (int h = 0; h < RBH; ++h)
 #pragma unroll
         for (int t = 0; t < BNB; ++t)
-            acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < a.ksplit; ++sp) {
-        uint64_t part[NW];
-        const uint64_t *src = wsp + (size_t)sp * TILE_W;
+            sum[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < a.ksplit; c0 += CH) {
+        uint64_t part[CH][NW];
 #pragma unroll
-        for (int r = 0; r < RBW; ++r)
+        for (int ci = 0; ci < CH; ++ci) {
+            // Splits past the end re-read the last one (valid memory, never summed).
+            const int sp = min(c0 + ci, a.ksplit - 1);
+            const uint64_t *src = wsp + (size_t)sp * TILE_W;
 #pragma unroll
-            for (int t = 0; t < BNB; ++t)
+            for (int h = 0; h < RBH; ++h)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    part[(r * BNB + t) * 2 + h] =
-                        __hip_atomic_load(src + word_of(r, t, h), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int t = 0; t < BNB; ++t)
 #pragma unroll
-        for (int r = 0; r < RBW; ++r)
+                    for (int w = 0; w < 2; ++w)
+                        part[ci][(h * BNB + t) * 2 + w] =
+                            __hip_atomic_load(src + word_of(h, t, w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
-            for (int t = 0; t < BNB; ++t) {
-                const uint64_t w0 = part[(r * BNB + t) * 2];
-                const uint64_t w1 = part[(r * BNB + t) * 2 + 1];
-                const u32x4 u = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
-                acc[r][t] += __builtin_bit_cast(f32x4, u);
-            }
+        for (int ci = 0; ci < CH; ++ci) {
+            const int sp = c0 + ci;
+            if (sp >= a.ksplit)
+                break;
+#pragma unroll
+            for (int h = 0; h < RBH; ++h)
+#pragma unroll
+                for (int t = 0; t < BNB; ++t) {
+                    if (sp == ks) {
+                        sum[h][t] += fin[h][t];          // same bits as the published copy
+                    } else {
+                        const uint64_t w0 = part[ci][(h * BNB + t) * 2];
+                        const uint64_t w1 = part[ci][(h * BNB + t) * 2 + 1];
+                        const u32x4 u = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+                        sum[h][t] += __builtin_bit_cast(f32x4, u);
+                    }
+                }
+        }
     }
 #pragma unroll
-    for (int r = 0; r < RBW; ++r)
+    for (int h = 0; h < RBH; ++h)
 #pragma unroll
         for (int t = 0; t < BNB; ++t)
-            store_out(r, t, acc[r][t]);
+            store_out(h, t, sum[h][t]);
     if (tid == 0)
         __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

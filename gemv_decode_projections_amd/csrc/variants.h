@@ -14,13 +14,13 @@ struct SkinnyVariant {
     const void *fn;   // __global__ void (SkinnyArgs)
 };
 
-// Tiled (large-m) kernel variants: BMB x BNB blocks of 16 per workgroup, WR x WC waves
-// (WR = waves, WC = 1: waves split the rows).
+// Tiled (large-m) kernel variants: BMB x BNB blocks of 16 per workgroup, WR waves
+// splitting the rows (KG = 1: every wave takes every k-step).
 struct TiledVariant {
     int bmb;
     int bnb;
     int wr;
-    int wc;
+    int kg;
     int depth;        // prefetch distance in k-steps
     int f32w;
     const void *fn;   // __global__ void (TiledArgs)

@@ -138,8 +138,9 @@ int proj_last_hip_error(void);
  *   rb        16-row blocks per workgroup (kinds 0, 1); rows per workgroup
  *             (kind 2)
  *   waves     wavefronts per workgroup (4 for kind 2)
- *   spw       k-steps of 32 per wave (kind 0); prefetch distance in k-steps
- *             (kind 1; the k-steps of one workgroup must be a multiple of it);
+ *   spw       k-steps of 32 per wave (kind 0); weight prefetch distance in
+ *             k-steps (kind 1; the k-steps of one workgroup must be a
+ *             multiple of it);
  *             k chunks of 2048 per row (kind 2: K = 2048 * spw)
  *   ksplit    workgroups that split K for one tile (1 = no cross-workgroup
  *             reduction; >1 = last-arriving workgroup sums the partials in
