@@ -16,7 +16,9 @@ outside the measured interval.
 A step is one decode-1 load (m = 1, all five layers, cold before each layer):
 the headline `value` is the median over the timed steps of the per-step sum.
 The other loads (decode-16/32, verify-1/16/32) are measured the same way and
-reported under `loads`. Inputs are seeded synthetic tensors already resident
+reported under `loads` (with achieved TB/s and TFLOP/s). `graph_replay`
+repeats every load with the pages' method (each call captured in a HIP graph,
+replayed cold, minus an empty-kernel graph) for context. Inputs are seeded synthetic tensors already resident
 in device memory; weights are prepared (repacked) before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -24,7 +26,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -38,6 +39,7 @@ if ROOT not in sys.path:
 
 FLUSH_BYTES = 1 << 30
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
 # Pages' H200 per-load time for decode 1, best reported (guide ch. 1 §1.8 table).
 H200_DECODE1_US = 38.25
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_decode1.json")
@@ -48,11 +50,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Sources that determine the decode-1 (m = 1) kernels and the weight layout
+# they read; the dispatch choice itself is checked by kernel name.
+DECODE1_SOURCES = ("common.h", "repack.h", "skinny.h", "rowdot.h", "skinny_bf16_nt1.hip", "skinny_bf16_nt2.hip",
+                   "skinny_f32.hip", "rowdot_variants.hip")
+
+
 def source_hash():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "gemv_decode_projections_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in DECODE1_SOURCES:
+        with open(os.path.join(ROOT, "gemv_decode_projections_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -97,6 +105,42 @@ class Bench:
         self.B.proj_bench_flush(self.flush, self.sink)
         self.B.proj_run_timed(layer, x, m, out, self.timer)
         return self.timer.elapsed_us()
+
+    def graph_us(self, layer, m, reps):
+        """Median cold time of one captured proj_run replayed as a HIP graph.
+
+        Events are recorded on the replay stream around graph.replay(), so the
+        time includes the graph launch overhead; graph_net_us subtracts the
+        same measurement of a graph holding one empty kernel.
+        """
+        torch, B = self.torch, self.B
+        x, out = self.xin(layer, m, 0) if layer is not None else (None, None)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            if layer is None:
+                B.proj_bench_empty(s)
+            else:
+                B.proj_run(layer, x, m, out, s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            if layer is None:
+                B.proj_bench_empty(s)
+            else:
+                B.proj_run(layer, x, m, out, s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            with torch.cuda.stream(s):
+                B.proj_bench_flush(self.flush, self.sink, s)
+                e0.record(s)
+                g.replay()
+                e1.record(s)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return statistics.median(ts)
 
     def floor_us(self, nbytes, reps):
         """Cold pure-read kernel over the same byte count (16-byte multiple)."""
@@ -152,11 +196,12 @@ def _cpu_name():
     return "unknown CPU"
 
 
-def traffic_for(layer, m):
+def traffic_for(layer, m, kernel=None):
     """HBM bytes per launch of (layer, m) from the committed counter summary.
 
-    None when there is no summary or the kernel sources changed since the
-    counters were read (the summary stores a hash of the sources).
+    None when there is no summary, the kernel sources changed since the
+    counters were read (the summary stores a hash of the sources), or the
+    dispatch now picks a different kernel for (layer, m).
     """
     try:
         with open(PMC_FILE) as f:
@@ -166,7 +211,7 @@ def traffic_for(layer, m):
     if d.get("source_hash") != source_hash():
         return None
     k = d.get("launches", {}).get("%s@%d" % (layer, m))
-    if not k:
+    if not k or (kernel is not None and k.get("kernel") != kernel):
         return None
     return int(round(k["fetch_bytes"] + k["write_bytes"]))
 
@@ -263,6 +308,8 @@ def main():
     ap.add_argument("--load-reps", type=int, default=20, help="cold calls per layer for the other loads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
+    ap.add_argument("--graph-reps", type=int, default=15)
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print per-layer durations of the timed steps from a rocprofv3 trace of bench.py")
@@ -329,12 +376,28 @@ def main():
             lay[layer] = round(t, 2)
         tot = sum(lay.values())
         nbytes = sum(rf.bytes_of(l, m) for l in layers)
+        flops = sum(rf.flops_of(l, m) for l in layers)
         loads[name] = {
             "m": m, "us": round(tot, 2), "layers_us": lay,
             "TBps": round(nbytes / tot / 1e6, 3),
+            "TFLOPs": round(flops / tot / 1e6, 2),
+            "mfma_frac": round(flops / tot / 1e6 / MFMA_BF16_TFLOPS, 4),
             "nominal_floor_us": round(rf.load_floor_us(m, router_peak=rf.MI355X_FP32_FLOPS), 2),
         }
         log("%-10s m=%-4d %8.2f us  %s" % (name, m, tot, lay))
+
+    # The pages' own timing method for context: each call captured in a HIP
+    # graph and replayed cold, minus the same for a graph of one empty kernel.
+    graph = None
+    if not args.no_graph:
+        empty = b.graph_us(None, 1, args.graph_reps)
+        graph = {"empty_graph_us": round(empty, 2), "loads": {}}
+        for name in LOAD_ORDER:
+            m = b.LOADS[name]
+            lay = {l: round(b.graph_us(l, m, args.graph_reps) - empty, 2) for l in layers}
+            graph["loads"][name] = {"m": m, "us_net": round(sum(lay.values()), 2), "layers_net_us": lay}
+        log("graph replay (net of an empty-kernel graph, %.2f us): %s" % (
+            empty, {k: v["us_net"] for k, v in graph["loads"].items()}))
 
     # Roofline of the dominant kernel of the headline load.
     dom = max(layers, key=lambda l: statistics.median(per_layer[l]))
@@ -345,7 +408,7 @@ def main():
     kname = kernel_name(cfg, dom == "router")
     roof = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dom, 1),
+        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dom, 1, kname),
         "kernel": kname, "layer": dom, "algorithmic_bytes": dom_bytes, "avg_us": round(dom_avg, 3),
         "measured_read_floor_us": round(floor[dom], 3),
         "frac_of_read_floor": round(floor[dom] / statistics.median(per_layer[dom]), 4),
@@ -379,6 +442,7 @@ def main():
         "decode1_frac_of_read_floor": round(floor_sum / value, 4),
         "decode1_TBps": round(sum(rf.bytes_of(l, 1) for l in layers) / value / 1e6, 3),
         "loads": loads,
+        "graph_replay": graph,
         "timed_wall_s": round(wall, 4),
         "roofline": roof,
         "cpu_baseline": cpu,

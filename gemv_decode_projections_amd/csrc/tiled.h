@@ -235,28 +235,46 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
     const int rbf = rbw0;                             // first row block of this wave
 
     // Epilogue. fin (h, t) covers rows (rbf + h)*16 + 4*(lane/16) + 0..3 and
-    // token tok0 + t*16 + lane%16.
-    auto store_out = [&](int h, int t, f32x4 v) {
-        const int tk = tok0 + t * 16 + (lane % 16);
-        if (tk >= a.m)
-            return;
-        const int row = (rbf + h) * kRowsPerBlock + 4 * (lane / 16);
-        if constexpr (F32W) {
-            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + (size_t)tk * a.n_eff + row) = v;
-        } else {
-            u32x2 p;
-            p.x = bf16_rne_bits(v.x) | (bf16_rne_bits(v.y) << 16);
-            p.y = bf16_rne_bits(v.z) | (bf16_rne_bits(v.w) << 16);
-            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + (size_t)tk * a.n_eff + row) = p;
+    // token tok0 + t*16 + lane%16. The tile is staged in LDS token-major (the
+    // activation ring is free after the last barrier) and written out in
+    // 16-byte chunks, consecutive lanes along one token's output row, so the
+    // stores are whole cache lines instead of 8-byte pieces on 16 rows.
+    constexpr int OB = F32W ? 4 : 2;                  // output bytes per element
+    constexpr int ROWB = BMB * kRowsPerBlock * OB;    // bytes of one token's tile row
+    constexpr int ROWP = ROWB + 16;                   // padded LDS row (bank skew)
+    constexpr int CPR = ROWB / 16;                    // 16-byte chunks per token row
+    static_assert(BNB * 16 * ROWP <= (int)sizeof(xl), "output tile must fit the activation ring");
+    char *ot = reinterpret_cast<char *>(&xl[0][0]);
+    auto store_tile = [&](f32x4 (&v)[RBH][BNB]) {
+#pragma unroll
+        for (int h = 0; h < RBH; ++h)
+#pragma unroll
+            for (int t = 0; t < BNB; ++t) {
+                const int tl = t * 16 + (lane % 16);
+                const int rl = (rbf - rt * BMB + h) * kRowsPerBlock + 4 * (lane / 16);
+                char *d = ot + tl * ROWP + rl * OB;
+                if constexpr (F32W) {
+                    *reinterpret_cast<f32x4 *>(d) = v[h][t];
+                } else {
+                    u32x2 p;
+                    p.x = bf16_rne_bits(v[h][t].x) | (bf16_rne_bits(v[h][t].y) << 16);
+                    p.y = bf16_rne_bits(v[h][t].z) | (bf16_rne_bits(v[h][t].w) << 16);
+                    *reinterpret_cast<u32x2 *>(d) = p;
+                }
+            }
+        __syncthreads();
+        char *obase = reinterpret_cast<char *>(a.out) + (size_t)rt * BMB * kRowsPerBlock * OB;
+        for (int c = tid; c < BNB * 16 * CPR; c += NTHR) {
+            const int tl = c / CPR, ck = c % CPR;
+            const int tk = tok0 + tl;
+            if (tk < a.m)
+                *reinterpret_cast<u32x4 *>(obase + (size_t)tk * a.n_eff * OB + ck * 16) =
+                    *reinterpret_cast<const u32x4 *>(ot + tl * ROWP + ck * 16);
         }
     };
 
     if (a.ksplit == 1) {
-#pragma unroll
-        for (int h = 0; h < RBH; ++h)
-#pragma unroll
-            for (int t = 0; t < BNB; ++t)
-                store_out(h, t, fin[h][t]);
+        store_tile(fin);
         return;
     }
 
@@ -339,11 +357,7 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
                 }
         }
     }
-#pragma unroll
-    for (int h = 0; h < RBH; ++h)
-#pragma unroll
-        for (int t = 0; t < BNB; ++t)
-            store_out(h, t, sum[h][t]);
+    store_tile(sum);
     if (tid == 0)
         __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
