@@ -299,11 +299,11 @@ proj_config plan_default(int layer, int m)
         int rb, nt, waves, depth, ksplit;
     };
     static const TEntry ttable[PROJ_NUM_LAYERS][3] = {
-        /* qkv_gate */ {{4, 4, 4, 4, 4}, {8, 4, 4, 16, 4}, {8, 4, 4, 16, 2}},
-        /* o        */ {{4, 4, 4, 4, 1}, {4, 4, 4, 4, 1}, {8, 4, 4, 4, 1}},
-        /* pooler   */ {{4, 4, 4, 8, 4}, {8, 4, 4, 16, 4}, {8, 4, 4, 16, 2}},
-        /* unpooler */ {{4, 4, 4, 4, 2}, {4, 4, 4, 4, 1}, {8, 4, 4, 16, 1}},
-        /* router   */ {{4, 4, 4, 4, 16}, {4, 4, 4, 4, 16}, {4, 4, 4, 4, 8}},
+        /* qkv_gate */ {{4, 2, 4, 16, 2}, {4, 2, 4, 16, 1}, {8, 2, 4, 8, 1}},
+        /* o        */ {{4, 2, 4, 8, 1}, {8, 2, 4, 8, 1}, {8, 4, 4, 4, 1}},
+        /* pooler   */ {{4, 2, 4, 8, 2}, {4, 2, 4, 16, 1}, {8, 2, 4, 8, 1}},
+        /* unpooler */ {{4, 2, 4, 8, 1}, {8, 2, 4, 8, 1}, {8, 4, 4, 16, 1}},
+        /* router   */ {{4, 2, 4, 4, 16}, {4, 2, 4, 4, 8}, {4, 2, 4, 4, 8}},
     };
     const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : 2)];
     const int ne = n_eff_of(layer, m);

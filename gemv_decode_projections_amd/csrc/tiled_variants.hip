@@ -17,9 +17,12 @@ const TiledVariant kTiledVariants[] = {
     GDP_TILED(2, 4, 4, 4, 0)
     GDP_TILED(2, 4, 4, 8, 0)
     GDP_TILED(2, 4, 4, 16, 0)
-    GDP_TILED(2, 8, 4, 8, 0)
+    GDP_TILED(1, 2, 4, 8, 0)
+    GDP_TILED(2, 2, 4, 8, 0)
+    GDP_TILED(1, 2, 4, 16, 0)
     GDP_TILED(1, 4, 4, 4, 1)
-    GDP_TILED(1, 4, 4, 8, 1)
+    GDP_TILED(1, 2, 4, 4, 1)
+    GDP_TILED(1, 2, 4, 8, 1)
 };
 const int kTiledVariantCount = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
 
