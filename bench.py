@@ -221,8 +221,9 @@ def kernel_name(cfg, f32w):
     f = "true" if f32w else "false"
     if cfg.kind == 0:
         return "skinny_kernel<%d, %d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.waves, cfg.spw, f)
-    if cfg.kind == 1:
-        return "tiled_kernel<%d, %d, %d, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.waves, cfg.spw, f)
+    if cfg.kind == 1:   # <rows per wave, token blocks, waves, k-steps per super-step, depth, fp32>
+        return "tiled_kernel<%d, %d, %d, %d, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.waves,
+                                                         min(4, cfg.spw // 2), cfg.spw, f)
     return "rowdot_kernel<%d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.spw, f)
 
 
@@ -253,6 +254,57 @@ def summarize_trace(trace_csv, steps, warmup):
         out[layer] = {"kernel": timed[i]["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
                       "grid": int(timed[i]["Grid_Size_X"]), "n": len(d),
                       "mean_us": round(statistics.mean(d), 3), "median_us": round(statistics.median(d), 3)}
+    return out
+
+
+def call_sequence(steps, warmup, load_reps, graph_reps, graph=True):
+    """(load, layer) of every projection kernel bench.py launches, in launch order."""
+    from workload import LAYERS
+
+    seq = [("decode-1", l) for _ in range(warmup + steps) for l in LAYERS]
+    for name in LOAD_ORDER[1:]:
+        for l in LAYERS:
+            seq += [(name, l)] * load_reps
+    if graph:
+        for name in LOAD_ORDER:
+            for l in LAYERS:
+                seq += [(name, l)] * (1 + graph_reps)   # one direct warm-up run, then the replays
+    return seq
+
+
+def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps):
+    """Kernel durations of every (load, layer) from a rocprofv3 kernel trace of bench.py.
+
+    The projection launches in the trace (in start order) are matched one to
+    one with the launch sequence of the bench run; the run's step, warm-up and
+    repetition counts must be the ones given here.
+    """
+    from gemv_decode_projections_amd import roofline as rf
+    from workload import LOADS
+
+    rows = sorted((r for r in _read_csv(trace_csv) if _is_proj_kernel(r["Kernel_Name"])),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    seq = call_sequence(steps, warmup, load_reps, graph_reps)
+    if len(rows) != len(seq):
+        raise SystemExit("trace has %d projection launches, the bench sequence %d: counts differ"
+                         % (len(rows), len(seq)))
+    per = {}
+    for (name, layer), r in zip(seq, rows):
+        e = per.setdefault((name, layer), {"kernel": r["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
+                                           "grid": int(r["Grid_Size_X"]), "d": []})
+        e["d"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = {}
+    for name in LOAD_ORDER:
+        m = LOADS[name]
+        lay = {}
+        for (n2, layer), e in per.items():
+            if n2 != name:
+                continue
+            med = statistics.median(e["d"])
+            lay[layer] = {"kernel": e["kernel"], "grid": e["grid"], "n": len(e["d"]), "median_us": round(med, 3),
+                          "TBps": round(rf.bytes_of(layer, m) / med / 1e6, 3),
+                          "TFLOPs": round(rf.flops_of(layer, m) / med / 1e6, 1)}
+        out[name] = {"m": m, "sum_median_us": round(sum(v["median_us"] for v in lay.values()), 2), "layers": lay}
     return out
 
 
@@ -313,12 +365,18 @@ def main():
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print per-layer durations of the timed steps from a rocprofv3 trace of bench.py")
+    ap.add_argument("--summarize-loads-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print per-(load, layer) kernel durations from a rocprofv3 trace of bench.py")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print HBM bytes per launch from the two --pmc passes")
     args = ap.parse_args()
 
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace, args.steps, args.warmup), indent=1))
+        return
+    if args.summarize_loads_trace:
+        print(json.dumps(summarize_loads_trace(args.summarize_loads_trace, args.steps, args.warmup, args.load_reps,
+                                               args.graph_reps), indent=1))
         return
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
