@@ -260,11 +260,11 @@ proj_config plan_default(int layer, int m)
         /* o         512 row blocks,  32 k-steps */
         {{1, 2, 4, 8, 1}, {1, 2, 4, 8, 1}, {2, 2, 4, 8, 1}},
         /* pooler    256 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {2, 2, 4, 32, 2}},
+        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {1, 2, 16, 16, 1}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
         {{1, 1, 8, 16, 1}, {1, 1, 4, 32, 1}, {2, 2, 4, 32, 1}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
-        {{1, 1, 8, 4, 8}, {1, 1, 16, 2, 8}, {2, 1, 16, 2, 8}},
+        {{1, 1, 8, 4, 8}, {1, 1, 16, 2, 8}, {1, 1, 8, 4, 8}},
     };
     proj_config c{};
     // Few tokens on the router (m <= 8) and the unpooler slice (m <= 4):

@@ -91,6 +91,20 @@ def test_awkward_m(wseed, m, layer, outliers):
     assert r.ok, r
 
 
+@pytest.mark.parametrize("layer", LAYERS)
+def test_max_token_count(layer):
+    """The largest m the library accepts (PROJ_MAX_M), checked on sampled rows
+    (every probe row, the first and last rows and random ones)."""
+    p = prepared(0)
+    m = binding.PROJ_MAX_M
+    xs = make_x(layer, m, seed=1100, outliers=True)
+    say("max m", layer, "m=%d" % m)
+    got = run_layer(layer, xs.bits)
+    assert np.all(np.isfinite(got))
+    r = compare(layer, got, p.w[layer], xs, sample_rows(xs, m))
+    assert r.ok, r
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 6, 11, 13, 15, 17, 20, 24, 31, 40, 48, 64, 100])
 def test_more_token_counts(m):
     p = prepared(0)
