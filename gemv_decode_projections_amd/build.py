@@ -24,6 +24,7 @@ SOURCES = [
     "skinny_f32.hip",
     "tiled_variants.hip",
     "rowdot_variants.hip",
+    "wide_variants.hip",
 ]
 
 ARCH = os.environ.get("GDP_OFFLOAD_ARCH", "gfx950")
@@ -44,6 +45,7 @@ COMMON = [
 # skinny kernels, so only here).
 EXTRA = {
     "tiled_variants.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "wide_variants.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -29,6 +29,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> packed BF16 bits (lo in bits 0..15), round to nearest,
+// ties to even: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // FP32 -> BF16 bits, round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 {

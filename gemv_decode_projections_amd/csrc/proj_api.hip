@@ -11,6 +11,7 @@
 #include "skinny.h"
 #include "tiled.h"
 #include "variants.h"
+#include "wide.h"
 
 namespace gdp {
 namespace {
@@ -94,6 +95,16 @@ const TiledVariant *find_tiled(int bmb, int bnb, int waves, int depth, int f32w)
     return nullptr;
 }
 
+const WideVariant *find_wide(int bmb, int bnb, int depth, int f32w)
+{
+    for (int i = 0; i < kWideVariantCount; ++i) {
+        const WideVariant &v = kWideVariants[i];
+        if (v.bmb == bmb && v.bnb == bnb && v.depth == depth && v.f32w == f32w)
+            return &v;
+    }
+    return nullptr;
+}
+
 const RowVariant *find_row(int mcap, int r, int kit, int f32w)
 {
     for (int i = 0; i < kRowVariantCount; ++i) {
@@ -106,7 +117,7 @@ const RowVariant *find_row(int mcap, int r, int kit, int f32w)
 
 int skinny_variants() { return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count; }
 
-int total_variants() { return skinny_variants() + kTiledVariantCount + kRowVariantCount; }
+int total_variants() { return skinny_variants() + kTiledVariantCount + kRowVariantCount + kWideVariantCount; }
 
 const SkinnyVariant *variant_at(int i)
 {
@@ -130,6 +141,7 @@ struct Launch {
     SkinnyArgs sargs;
     TiledArgs targs;
     RowArgs rargs;
+    WideArgs wargs;
     int grid;
     int block;
 };
@@ -221,6 +233,46 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
         return PROJ_OK;
     }
+    if (c.kind == 3) {
+        // rb = 16-row blocks per tile (4 waves x rb/4), nt = 16-token blocks,
+        // spw = weight prefetch depth in k-steps; K split unevenly in
+        // super-steps of 2 k-steps.
+        const WideVariant *v = find_wide(c.rb, c.nt, c.spw, f32w);
+        if (!v || c.waves != 4)
+            return PROJ_ERR_UNSUPPORTED;
+        if (ne % (kRowsPerBlock * c.rb) != 0 || c.ksplit > KS / 2)
+            return PROJ_ERR_UNSUPPORTED;
+        const int n_rt = ne / (kRowsPerBlock * c.rb);
+        const int n_tt = (m + 16 * c.nt - 1) / (16 * c.nt);
+        const long long grid = (long long)n_rt * n_tt * c.ksplit;
+        if (grid < 1 || grid > 0x7fffffffLL)
+            return PROJ_ERR_UNSUPPORTED;
+        if (c.ksplit > 1) {
+            const long long tile_bytes = (long long)c.rb * c.nt * kWave * 16;
+            if ((long long)n_rt * n_tt * c.ksplit * tile_bytes > (long long)kWsBytes)
+                return PROJ_ERR_UNSUPPORTED;
+            if ((long long)n_rt * n_tt > (long long)kCounters)
+                return PROJ_ERR_UNSUPPORTED;
+        }
+        L.fn = v->fn;
+        L.kind = 3;
+        L.grid = (int)grid;
+        L.block = 4 * kWave;
+        WideArgs &A = L.wargs;
+        A.wp = st.wp;
+        A.zrow = st.zrow;
+        A.ws = reinterpret_cast<float *>(st.ws);
+        A.ws_bytes = (uint32_t)kWsBytes;
+        A.counters = st.counters;
+        A.m = m;
+        A.K = li.K;
+        A.n_eff = ne;
+        A.n_rt = n_rt;
+        A.n_tt = n_tt;
+        A.ksplit = c.ksplit;
+        A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
+        return PROJ_OK;
+    }
     if (c.kind == 2) {
         // nt = token capacity, rb = rows per workgroup, spw = 2048-wide k chunks per row
         const RowVariant *v = find_row(c.nt, c.rb, c.spw, f32w);
@@ -290,32 +342,33 @@ proj_config plan_default(int layer, int m)
         c.ksplit = e.ksplit;
         return c;
     }
-    // Larger m: tiled kernel, picked per layer from measured sweeps. Buckets:
-    // m <= 64, m <= 128, larger. Entries: row blocks (rb), token blocks (nt),
-    // waves, weight prefetch depth in k-steps, K split. Past 256 tokens the split halves until
-    // the grid is at most ~3 workgroups per compute unit and the partials fit
-    // the workspace.
+    // Larger m: the tiled kernel (kind 1) or the wide-tile kernel (kind 3),
+    // picked per layer from measured cold-cache sweeps. Buckets: m <= 64,
+    // m <= 128, larger. Entries: kind, 16-row blocks per tile (rb), 16-token
+    // blocks (nt), weight prefetch depth in k-steps, K split. Past 256 tokens
+    // the split shrinks until the grid is at most ~3 workgroups per compute
+    // unit and the partials fit the workspace.
     struct TEntry {
-        int rb, nt, waves, depth, ksplit;
+        int kind, rb, nt, depth, ksplit;
     };
     static const TEntry ttable[PROJ_NUM_LAYERS][3] = {
-        /* qkv_gate */ {{4, 2, 4, 16, 2}, {4, 2, 4, 16, 1}, {8, 2, 4, 8, 1}},
-        /* o        */ {{4, 2, 4, 8, 1}, {8, 2, 4, 8, 1}, {8, 4, 4, 4, 1}},
-        /* pooler   */ {{4, 2, 4, 8, 2}, {4, 2, 4, 16, 1}, {8, 2, 4, 8, 1}},
-        /* unpooler */ {{4, 2, 4, 8, 1}, {8, 2, 4, 8, 1}, {8, 4, 4, 16, 1}},
-        /* router   */ {{4, 2, 4, 4, 16}, {4, 2, 4, 4, 8}, {4, 2, 4, 4, 8}},
+        /* qkv_gate */ {{3, 4, 2, 8, 3}, {3, 4, 4, 8, 3}, {3, 8, 4, 8, 3}},
+        /* o        */ {{1, 4, 2, 8, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 4, 1}},
+        /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 8, 2}},
+        /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 8, 1}},
+        /* router   */ {{1, 4, 2, 8, 16}, {1, 4, 2, 4, 8}, {1, 4, 2, 4, 8}},
     };
     const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : 2)];
     const int ne = n_eff_of(layer, m);
-    c.kind = 1;
+    c.kind = e.kind;
     c.rb = e.rb;
     c.nt = e.nt;
-    c.waves = e.waves;
+    c.waves = 4;
     c.spw = e.depth;
     const long tiles = (long)(ne / (16 * c.rb)) * ((m + 16 * c.nt - 1) / (16 * c.nt));
     int ks = e.ksplit;
     while (ks > 1 && (tiles * ks > 768 || tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes))
-        ks /= 2;
+        ks = e.kind == 3 ? ks - 1 : ks / 2;   // the tiled kernel splits K into equal powers of two
     c.ksplit = ks;
     return c;
 }
@@ -350,11 +403,13 @@ int launch(const Launch &L, const void *x, void *out, hipStream_t stream, hipEve
     SkinnyArgs sargs = L.sargs;
     TiledArgs targs = L.targs;
     RowArgs rargs = L.rargs;
-    sargs.x = targs.x = rargs.x = static_cast<const uint16_t *>(x);
-    sargs.out = targs.out = rargs.out = out;
+    WideArgs wargs = L.wargs;
+    sargs.x = targs.x = rargs.x = wargs.x = static_cast<const uint16_t *>(x);
+    sargs.out = targs.out = rargs.out = wargs.out = out;
     void *params[1];
     params[0] = L.kind == 0   ? static_cast<void *>(&sargs)
                 : L.kind == 1 ? static_cast<void *>(&targs)
+                : L.kind == 3 ? static_cast<void *>(&wargs)
                               : static_cast<void *>(&rargs);
     hipError_t e;
     if (ev_start || ev_stop)
@@ -553,7 +608,25 @@ int proj_num_variants(void) { return total_variants(); }
 
 int proj_variant(int i, int *is_f32w, proj_config *cfg)
 {
-    if (i >= skinny_variants() + kTiledVariantCount && i < total_variants()) {
+    const int wide0 = skinny_variants() + kTiledVariantCount + kRowVariantCount;
+    if (i >= wide0 && i < total_variants()) {
+        const WideVariant &w = kWideVariants[i - wide0];
+        if (is_f32w)
+            *is_f32w = w.f32w;
+        if (cfg) {
+            proj_config c{};
+            c.kind = 3;
+            c.nt = w.bnb;
+            c.rb = w.bmb;
+            c.waves = 4;
+            c.spw = w.depth;
+            c.ksplit = 1;
+            c.block = 4 * kWave;
+            *cfg = c;
+        }
+        return PROJ_OK;
+    }
+    if (i >= skinny_variants() + kTiledVariantCount && i < wide0) {
         const RowVariant &r = kRowVariants[i - skinny_variants() - kTiledVariantCount];
         if (is_f32w)
             *is_f32w = r.f32w;

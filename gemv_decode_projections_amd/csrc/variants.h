@@ -35,6 +35,16 @@ struct RowVariant {
     const void *fn;   // __global__ void (RowArgs)
 };
 
+// Wide-tile (large-m, split-K) kernel variants: BMB = 4*RBW row blocks x BNB
+// token blocks per workgroup of 4 waves.
+struct WideVariant {
+    int bmb;
+    int bnb;
+    int depth;        // weight prefetch distance in k-steps
+    int f32w;
+    const void *fn;   // __global__ void (WideArgs)
+};
+
 // Each part is defined in its own translation unit so the variants compile in parallel.
 extern const SkinnyVariant kSkinnyPartBf16Nt1[];
 extern const int kSkinnyPartBf16Nt1Count;
@@ -44,6 +54,8 @@ extern const SkinnyVariant kSkinnyPartF32[];
 extern const int kSkinnyPartF32Count;
 extern const TiledVariant kTiledVariants[];
 extern const int kTiledVariantCount;
+extern const WideVariant kWideVariants[];
+extern const int kWideVariantCount;
 extern const RowVariant kRowVariants[];
 extern const int kRowVariantCount;
 

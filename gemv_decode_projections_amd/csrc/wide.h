@@ -1,0 +1,380 @@
+// Wide-tile MFMA kernel: out = x @ W^T when many tokens share each weight
+// byte (m >= 33; the pages' verify loads run m = 128 and 256, guide ch. 1
+// "The problem, the judge and the speed of light", §1.2, and only there does
+// the math approach the memory time, §1.7).
+//
+// The report "Muse Spark Open Kernel Challenge - muse_bf16_proj" (round 4)
+// traced its dense-layer losses to activations re-read by every row tile and
+// to per-block ingest. Measured on MI355X, the main loop of this kernel moves
+// ~30 bytes per clock per compute unit through L2 whatever the tile shape (the
+// L2 channels are 70-80 % busy), so the time goes with the bytes a tile
+// pulls in: 64 (R + T) per 32-wide k-step for an R x T tile. Large tiles pull
+// fewer bytes per multiply but leave too few tiles to fill 256 compute units,
+// so K is split over workgroups and the partial tiles are summed by the last
+// workgroup to finish.
+//
+// gfx950 design:
+//   * A workgroup (4 waves) owns 4*RBW 16-row blocks x BNB 16-token blocks
+//     and a range of k-steps. Wave w owns RBW row blocks and every token
+//     block, so each weight byte is loaded by exactly one wave.
+//   * Weights (the HBM stream) go straight into registers from the
+//     fragment-major packing (repack.h), each wave reading 1 KB contiguous
+//     per load, D k-steps ahead of use.
+//   * Activations are staged through a 4-slot LDS ring in super-steps of S
+//     k-steps: consecutive lanes read one token's contiguous S*64 bytes two
+//     super-steps ahead and write them where the MFMA B operand is read
+//     (lane l: token l%16, k = 8*(l/16)+0..7), rotated per token so that
+//     the reads of one 16-lane phase hit 16 distinct 16-byte bank groups.
+//     One barrier per super-step.
+//   * B fragments are double-buffered in registers: the next k-step's are
+//     read from LDS one at a time between the current k-step's MFMAs
+//     (explicit scheduling groups; at one wave per SIMD nothing else hides
+//     the LDS latency).
+//   * K may be split unevenly over KSPLIT workgroups (split lengths differ
+//     by at most one super-step); the split index varies fastest across
+//     workgroups, so one tile's workgroups sit on one XCD. Partials are
+//     published with write-through 16-byte stores, the arrival is counted
+//     with a device-scope atomic, and the last workgroup sums all splits in
+//     split order (deterministic) with coherent loads. (Keeping the partials
+//     in the XCD's L2 instead measured no faster: the last workgroup's gather
+//     is bound by its own compute unit's ingest, and the weight stream
+//     evicts the partials from L2.)
+//   * Token rows past m read a library-owned zero row and are never stored;
+//     loads past the end of the K range are clamped to its last k-step
+//     (cache hits, never consumed).
+#pragma once
+
+#include "common.h"
+
+namespace gdp {
+
+struct WideArgs {
+    const void *wp;          // packed weights
+    const uint16_t *x;       // m x K BF16
+    const uint16_t *zrow;    // K zero BF16 values (library-owned)
+    void *out;               // m x n_eff
+    float *ws;               // split-K partials
+    uint32_t *counters;      // per-tile arrival counters, zero between launches
+    uint32_t ws_bytes;       // size of ws (bounds of the buffer descriptor)
+    int m;
+    int K;
+    int n_eff;
+    int n_rt;                // row tiles
+    int n_tt;                // token tiles
+    int ksplit;
+    int xcd_remap;
+};
+
+// Raw buffer descriptor over [p, p + bytes) (gfx9 dword 3: 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache policy bits of buffer accesses on gfx950: sc1 makes a store write
+// through to memory and a load fetch from it, so accesses from different
+// XCDs (each with its own L2) see one another.
+constexpr int kCoherent = 16;
+
+template <int RBW, int BNB, int D, int S, bool F32W>
+__global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
+{
+    constexpr int WAVES = 4;
+    constexpr int NTHR = WAVES * kWave;
+    constexpr int AW = F32W ? 2 : 1;                  // 1 KB units per weight fragment
+    constexpr int BMB = WAVES * RBW;                  // row blocks per tile
+    constexpr int PAD = 4;                            // units between k-step regions (write skew)
+    constexpr int REG = BNB * kWave + PAD;            // LDS units per k-step region
+    constexpr int UNITS = S * BNB * kWave;            // 16-byte activation units per super-step
+    constexpr int CPT = 4 * S;                        // 16-byte chunks per token per super-step
+    static_assert(S == 1 || S == 2 || S == 4, "k-steps per super-step");
+    static_assert(D % S == 0 && ((D / S) % 2) == 0, "the unrolled pass holds an even number of super-steps");
+    static_assert(D / S <= 4, "the tail (fewer than D/S super-steps) must need no activation loads");
+    static_assert(UNITS % NTHR == 0, "activation units must split over threads");
+    constexpr int XPT = UNITS / NTHR;                 // activation units per thread per super-step
+
+    constexpr int OB = F32W ? 4 : 2;                  // output bytes per element
+    constexpr int ROWB = BMB * kRowsPerBlock * OB;    // bytes of one token's tile row
+    constexpr int ROWP = ROWB + 16;                   // padded LDS row (bank skew)
+    constexpr int RING = 4 * S * REG * 16;
+    constexpr int STAGE = BNB * 16 * ROWP;
+    constexpr int LDSB = RING > STAGE ? RING : STAGE;
+    __shared__ __attribute__((aligned(16))) char lds[LDSB];
+    __shared__ int s_last;
+    u32x4 *xl = reinterpret_cast<u32x4 *>(lds);
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+
+    // Workgroup -> (split, token tile, row tile), split fastest.
+    const int G = gridDim.x;
+    int L = blockIdx.x;
+    if (a.xcd_remap)
+        L = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+    const int ks = L % a.ksplit;
+    const int rest = L / a.ksplit;
+    const int tt = rest % a.n_tt;
+    const int rt = rest / a.n_tt;
+
+    const int KS = a.K / kStepK;
+    const int NSS = KS / S;                           // super-steps in the whole row
+    const int tok0 = tt * BNB * 16;
+    const int rbw0 = rt * BMB + wave * RBW;           // first row block of this wave
+
+    const u32x4 *wbase = reinterpret_cast<const u32x4 *>(a.wp);
+
+    // Activation load plan: unit u of a super-step is chunk c = u % CPT of
+    // token u / CPT, so consecutive lanes read one token's S*64 contiguous
+    // bytes. Chunk c is k-step c/4, k-group c%4 of the super-step.
+    const uint16_t *xsrc[XPT];
+    int xdst[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int u = i * NTHR + tid;
+        const int c = u % CPT;
+        const int qt = u / CPT;                       // token within the tile
+        const int blk = qt / 16, q = qt % 16;
+        const int sub = c / 4, g = c % 4;
+        const int tok = tok0 + qt;
+        xsrc[i] = (tok < a.m ? a.x + (size_t)tok * a.K : a.zrow) + 8 * c;
+        xdst[i] = sub * REG + blk * kWave + 4 * q + ((g + q / 4) & 3);
+    }
+    // LDS unit holding (token l%16, k-group l/16) of a fragment for this lane.
+    const int bslot = 4 * (lane % 16) + (((lane / 16) + (lane % 16) / 4) & 3);
+
+    f32x4 acc[RBW][BNB];
+
+    // acc = the partial product over super-steps [ss0, ss0 + nss) (nss >= 1).
+    auto run = [&](int ss0, int nss) {
+        const int steps = nss * S;
+        const int step0 = ss0 * S;
+        u32x4 wr[D][RBW][AW];
+        u32x4 xr[2][XPT];
+        u32x4 br[2][BNB];
+#pragma unroll
+        for (int r = 0; r < RBW; ++r)
+#pragma unroll
+            for (int t = 0; t < BNB; ++t)
+                acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        auto load_w = [&](int slot, int j) {          // k-step j of the range
+            const int st = step0 + (j < steps ? j : steps - 1);
+#pragma unroll
+            for (int r = 0; r < RBW; ++r) {
+                const u32x4 *f = wbase + ((size_t)(rbw0 + r) * KS + st) * (AW * kWave) + lane;
+#pragma unroll
+                for (int h = 0; h < AW; ++h)
+                    wr[slot][r][h] = f[h * kWave];
+            }
+        };
+        auto load_x = [&](int slot, int J) {          // super-step J
+            const int st = step0 + (J < nss ? J : nss - 1) * S;
+#pragma unroll
+            for (int i = 0; i < XPT; ++i)
+                xr[slot][i] = *reinterpret_cast<const u32x4 *>(xsrc[i] + (size_t)st * kStepK);
+        };
+        auto store_x = [&](int slot, int buf) {
+#pragma unroll
+            for (int i = 0; i < XPT; ++i)
+                xl[buf * S * REG + xdst[i]] = xr[slot][i];
+        };
+        // One k-step: multiply the weight fragments in ring slot `slot` with
+        // the B fragments in br[cur] while the next k-step's B fragments are
+        // read from LDS (buf, sub) into br[cur ^ 1], one LDS read after each
+        // token block's MFMAs.
+        auto kstep = [&](int slot, int cur, int buf, int sub) {
+            u32x4 a0[RBW], a1[RBW], a2[RBW];
+#pragma unroll
+            for (int r = 0; r < RBW; ++r) {
+                if constexpr (F32W)
+                    split3_f32(wr[slot][r][0], wr[slot][r][1], a0[r], a1[r], a2[r]);
+                else
+                    a0[r] = wr[slot][r][0];
+            }
+#pragma unroll
+            for (int t = 0; t < BNB; ++t) {
+#pragma unroll
+                for (int r = 0; r < RBW; ++r) {
+                    acc[r][t] = mfma16x16x32(a0[r], br[cur][t], acc[r][t]);
+                    if constexpr (F32W) {
+                        acc[r][t] = mfma16x16x32(a1[r], br[cur][t], acc[r][t]);
+                        acc[r][t] = mfma16x16x32(a2[r], br[cur][t], acc[r][t]);
+                    }
+                }
+                br[cur ^ 1][t] = xl[(buf * S + sub) * REG + t * kWave + bslot];
+            }
+#pragma unroll
+            for (int t = 0; t < BNB; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, F32W ? 3 * RBW : RBW, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // LDS read
+            }
+        };
+
+        // Pipeline. Weights: register ring of D k-steps; k-step j+D is
+        // loaded while k-step j is multiplied. Activations: super-step J+2
+        // waits in registers (loaded two super-steps earlier) and is written
+        // to LDS slot (J+2)%4 at the end of super-step J; super-step J+4 is
+        // loaded in its place. The barrier that ends super-step J publishes
+        // slot (J+2)%4 and retires every read of the slot that super-step
+        // J+1 overwrites (last read during super-step J-2). The first B
+        // fragments of super-step J+1 are read during the last k-step of J
+        // (slot (J+1)%4, published by the barrier ending J-1).
+        load_x(0, 0);
+        load_x(1, 1);
+        store_x(0, 0);
+        store_x(1, 1);
+        load_x(0, 2);
+        load_x(1, 3);
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            load_w(j, j);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < BNB; ++t)
+            br[0][t] = xl[t * kWave + bslot];
+
+        // One k-step of the pipeline; `loads` is false in the tail, where
+        // every remaining operand is already in flight: weights are D
+        // k-steps ahead, and activations four super-steps ahead, which
+        // covers a tail of at most three super-steps (D/S <= 4): the data
+        // its LDS stores publish were loaded before the tail began.
+        auto body = [&](int jj, int j, bool loads) {
+            const int J = j / S;                      // super-step of k-step j
+            const int sub = jj % S;
+            if (sub + 1 < S)
+                kstep(jj, jj & 1, J & 3, sub + 1);
+            else
+                kstep(jj, jj & 1, (J + 1) & 3, 0);
+            if (loads)
+                load_w(jj, j + D);
+            if (sub == S - 1) {
+                const int xs = (jj / S) & 1;          // == J & 1: j0 / S is even
+                store_x(xs, (J + 2) & 3);
+                if (loads)
+                    load_x(xs, J + 4);
+                __syncthreads();
+            }
+        };
+        // Whole passes of D k-steps without branches (a branch around loads
+        // makes the compiler wait for every load in flight at the join), then
+        // the tail of fewer than D k-steps.
+        int j0 = 0;
+        for (; j0 + D <= steps; j0 += D) {
+#pragma unroll
+            for (int jj = 0; jj < D; ++jj)
+                body(jj, j0 + jj, true);
+        }
+        const int rem = steps - j0;
+#pragma unroll
+        for (int jj = 0; jj < D - S; ++jj)
+            if (jj < rem)
+                body(jj, j0 + jj, false);
+    };
+
+    // This split's super-steps.
+    const int ss_begin = (int)(((long)ks * NSS) / a.ksplit);
+    const int ss_count = (int)(((long)(ks + 1) * NSS) / a.ksplit) - ss_begin;
+    run(ss_begin, ss_count);
+
+    const int tile = rt * a.n_tt + tt;
+    if (a.ksplit > 1) {
+        // Publish this split's partial tile (write-through 16-byte stores,
+        // each wave's stores 1 KB contiguous), wait until they are complete,
+        // count the arrival; the last workgroup of the tile sums the splits.
+        // acc (r, t) covers rows (rbw0 + r)*16 + 4*(lane/16) + 0..3 and
+        // token tok0 + t*16 + lane%16.
+        constexpr int TILE_U = BMB * BNB * kWave;     // 16-byte words per partial tile
+        const uint32_t tile_off = (uint32_t)tile * a.ksplit * TILE_U * 16u;
+        auto unit_of = [&](int r, int t) { return ((wave * RBW + r) * BNB + t) * kWave + lane; };
+        const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(a.ws, a.ws_bytes);
+#pragma unroll
+        for (int r = 0; r < RBW; ++r)
+#pragma unroll
+            for (int t = 0; t < BNB; ++t)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[r][t]), ws,
+                                                       tile_off + ((uint32_t)ks * TILE_U + unit_of(r, t)) * 16u,
+                                                       0, kCoherent);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t prev =
+                __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(a.ksplit - 1));
+            if (s_last)
+                __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
+        // Sum in split order; this workgroup's own split comes from registers
+        // (the same bits it published). CH splits are gathered per round
+        // with every load in flight.
+        constexpr int CH = (RBW * BNB >= 16) ? 2 : (RBW * BNB >= 8 ? 4 : 8);
+        f32x4 sum[RBW][BNB];
+#pragma unroll
+        for (int r = 0; r < RBW; ++r)
+#pragma unroll
+            for (int t = 0; t < BNB; ++t)
+                sum[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 < a.ksplit; c0 += CH) {
+            u32x4 part[CH][RBW][BNB];
+#pragma unroll
+            for (int ci = 0; ci < CH; ++ci) {
+                const int sp = min(c0 + ci, a.ksplit - 1);   // past the end: re-read, never summed
+#pragma unroll
+                for (int r = 0; r < RBW; ++r)
+#pragma unroll
+                    for (int t = 0; t < BNB; ++t)
+                        part[ci][r][t] = __builtin_amdgcn_raw_buffer_load_b128(
+                            ws, tile_off + ((uint32_t)sp * TILE_U + unit_of(r, t)) * 16u, 0, kCoherent);
+            }
+#pragma unroll
+            for (int ci = 0; ci < CH; ++ci) {
+                const int sp = c0 + ci;
+                if (sp >= a.ksplit)
+                    break;
+#pragma unroll
+                for (int r = 0; r < RBW; ++r)
+#pragma unroll
+                    for (int t = 0; t < BNB; ++t)
+                        sum[r][t] += (sp == ks) ? acc[r][t] : __builtin_bit_cast(f32x4, part[ci][r][t]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RBW; ++r)
+#pragma unroll
+            for (int t = 0; t < BNB; ++t)
+                acc[r][t] = sum[r][t];
+    }
+
+    // Stage the output tile token-major in LDS and write whole 16-byte
+    // chunks along each token's output row. The barrier retires the last
+    // reads of the activation ring.
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RBW; ++r)
+#pragma unroll
+        for (int t = 0; t < BNB; ++t) {
+            const int tl = t * 16 + (lane % 16);
+            const int rl = (wave * RBW + r) * kRowsPerBlock + 4 * (lane / 16);
+            char *d = lds + tl * ROWP + rl * OB;
+            if constexpr (F32W)
+                *reinterpret_cast<f32x4 *>(d) = acc[r][t];
+            else
+                *reinterpret_cast<u32x2 *>(d) = u32x2{pack_bf16x2(acc[r][t].x, acc[r][t].y),
+                                                      pack_bf16x2(acc[r][t].z, acc[r][t].w)};
+        }
+    __syncthreads();
+    constexpr int CPR = ROWB / 16;                    // 16-byte chunks per token row
+    char *obase = reinterpret_cast<char *>(a.out) + (size_t)rt * BMB * kRowsPerBlock * OB;
+    for (int c = tid; c < BNB * 16 * CPR; c += NTHR) {
+        const int tl = c / CPR, ck = c % CPR;
+        const int tk = tok0 + tl;
+        if (tk < a.m)
+            *reinterpret_cast<u32x4 *>(obase + (size_t)tk * a.n_eff * OB + ck * 16) =
+                *reinterpret_cast<const u32x4 *>(lds + tl * ROWP + ck * 16);
+    }
+}
+
+}  // namespace gdp

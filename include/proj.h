@@ -129,18 +129,21 @@ int proj_last_hip_error(void);
  *
  * A configuration names one compiled kernel variant plus its split:
  *   kind      0 = skinny MFMA kernel (16-row blocks, waves split K in the
- *               workgroup), 1 = tiled MFMA kernel (large m; weight and
- *               activation tiles staged in LDS), 2 = row-dot kernel (m <= 8,
- *               router and the unpooler's 1024-row slice only: whole rows per
- *               workgroup from a row-major weight copy, FP32 multiply-adds)
- *   nt        token sub-tiles of 16 per workgroup (kinds 0, 1); largest token
+ *               workgroup), 1 = tiled MFMA kernel (large m; weights streamed
+ *               into registers, activation tiles staged in LDS), 2 = row-dot
+ *               kernel (m <= 8, router and the unpooler's 1024-row slice
+ *               only: whole rows per workgroup from a row-major weight copy,
+ *               FP32 multiply-adds), 3 = wide-tile MFMA kernel (large m;
+ *               4 waves, up to 128 x 128 tiles, K split unevenly over up to
+ *               KS/2 workgroups)
+ *   nt        token sub-tiles of 16 per workgroup (kinds 0, 1, 3); largest token
  *             count of the variant (kind 2)
- *   rb        16-row blocks per workgroup (kinds 0, 1); rows per workgroup
- *             (kind 2)
- *   waves     wavefronts per workgroup (4 for kind 2)
+ *   rb        16-row blocks per workgroup (kinds 0, 1, 3; a multiple of 4
+ *             for kind 3); rows per workgroup (kind 2)
+ *   waves     wavefronts per workgroup (4 for kinds 2 and 3)
  *   spw       k-steps of 32 per wave (kind 0); weight prefetch distance in
- *             k-steps (kind 1; the k-steps of one workgroup must be a
- *             multiple of it);
+ *             k-steps (kind 1: the k-steps of one workgroup must be a
+ *             multiple of it; kind 3: 4 or 8, any split);
  *             k chunks of 2048 per row (kind 2: K = 2048 * spw)
  *   ksplit    workgroups that split K for one tile (1 = no cross-workgroup
  *             reduction; >1 = last-arriving workgroup sums the partials in

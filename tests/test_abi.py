@@ -82,9 +82,13 @@ def test_dispatch_plans_tile_every_layer(lib):
                 continue
             if cfg.kind == 0:
                 assert cfg.waves * cfg.spw * cfg.ksplit == k // 32
-            else:
-                assert cfg.kind == 1 and (k // 32) % (cfg.spw * cfg.ksplit) == 0
+            elif cfg.kind == 1:
+                assert (k // 32) % (cfg.spw * cfg.ksplit) == 0
                 assert m > 32
+            else:
+                # wide tiles: 4 waves, whole 64-row blocks, any split up to one super-step each
+                assert cfg.kind == 3 and m > 32 and cfg.waves == 4 and cfg.rb % 4 == 0
+                assert 1 <= cfg.ksplit <= k // 64
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
             assert cfg.grid == ne // (16 * cfg.rb) * n_tt * cfg.ksplit

@@ -133,10 +133,15 @@ def _variant_cases():
                     split = ks // (cfg.waves * cfg.spw)
                     cases.append((layer, 0, cfg.nt, cfg.rb, cfg.waves, cfg.spw, split, 0))
                     break
-            elif n % (16 * cfg.rb) == 0:
+            elif cfg.kind == 1 and n % (16 * cfg.rb) == 0:
                 cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 1, 0))
                 cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 2, 0))
                 cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 2, 1))  # split groups across XCDs
+                break
+            elif cfg.kind == 3 and n % (16 * cfg.rb) == 0:
+                cases.append((layer, 3, cfg.nt, cfg.rb, 4, cfg.spw, 1, 0))
+                cases.append((layer, 3, cfg.nt, cfg.rb, 4, cfg.spw, 3, 0))   # uneven split lengths
+                cases.append((layer, 3, cfg.nt, cfg.rb, 4, cfg.spw, 5, 1))   # uneven, groups across XCDs
                 break
     return cases
 
@@ -147,14 +152,14 @@ def test_every_compiled_variant(case):
     p = prepared(0)
     if kind == 0:
         ms = [1, 16 * nt - 3, 16 * nt + 5]
-    elif kind == 1:
+    elif kind in (1, 3):
         ms = [33, 16 * nt + 5, 3 * 16 * nt - 7]
     else:
         ms = [1, nt // 2 + 1, nt]      # row-dot: up to its token capacity
     for m in sorted(set(ms)):
         if layer == "unpooler" and m > 8 and kind == 0:
             continue
-        if kind == 1 and split > 1:
+        if kind in (1, 3) and split > 1:
             n_tiles = (SHAPES[layer][0] // (16 * rb)) * -(-m // (16 * nt))
             if n_tiles * split * rb * nt * 1024 > WS_BYTES:
                 continue  # the library rejects it: split-K workspace is 32 MB per layer
