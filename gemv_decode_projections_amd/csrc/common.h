@@ -39,15 +39,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// FP32 -> BF16 bits, round to nearest, ties to even (NaN stays NaN).
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f)
-{
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
 
 // Exact three-way split of eight FP32 weights into BF16 parts, w = hi + mid + lo.
 // hi keeps the top 8 significand bits (truncation), mid the next 8 of the

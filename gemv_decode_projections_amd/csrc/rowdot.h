@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kRowThreads) void rowdot_kernel(RowArgs a)
             if constexpr (F32W)
                 static_cast<float *>(a.out)[o] = s;
             else
-                static_cast<uint16_t *>(a.out)[o] = (uint16_t)bf16_rne_bits(s);
+                static_cast<uint16_t *>(a.out)[o] = (uint16_t)pack_bf16x2(s, 0.f);
         }
     }
 }

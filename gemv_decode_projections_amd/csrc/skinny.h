@@ -220,8 +220,8 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + (size_t)tk * a.n_eff + row) = v;
         } else {
             u32x2 p;
-            p.x = bf16_rne_bits(v.x) | (bf16_rne_bits(v.y) << 16);
-            p.y = bf16_rne_bits(v.z) | (bf16_rne_bits(v.w) << 16);
+            p.x = pack_bf16x2(v.x, v.y);
+            p.y = pack_bf16x2(v.z, v.w);
             *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + (size_t)tk * a.n_eff + row) = p;
         }
     };

@@ -257,8 +257,8 @@ __global__ __launch_bounds__(WAVES * kWave) void tiled_kernel(TiledArgs a)
                     *reinterpret_cast<f32x4 *>(d) = v[h][t];
                 } else {
                     u32x2 p;
-                    p.x = bf16_rne_bits(v[h][t].x) | (bf16_rne_bits(v[h][t].y) << 16);
-                    p.y = bf16_rne_bits(v[h][t].z) | (bf16_rne_bits(v[h][t].w) << 16);
+                    p.x = pack_bf16x2(v[h][t].x, v[h][t].y);
+                    p.y = pack_bf16x2(v[h][t].z, v[h][t].w);
                     *reinterpret_cast<u32x2 *>(d) = p;
                 }
             }
