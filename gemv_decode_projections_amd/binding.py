@@ -71,6 +71,7 @@ def _lib():
         "proj_out_cols": ([i, i], i),
         "proj_layer_dims": ([i, ip, ip, ip, ip], i),
         "proj_release": ([i], i),
+        "proj_compressed": ([i], i),
         "proj_strerror": ([i], ctypes.c_char_p),
         "proj_last_hip_error": ([], i),
         "proj_plan": ([i, i, cp], i),
@@ -157,6 +158,14 @@ def proj_run_config(layer, x, m, out, cfg, stream=None):
     _check(_lib().proj_run_config(_layers.layer_id(layer), _ptr(x), int(m), _ptr(out), _stream(stream),
                                   ctypes.byref(cfg)),
            "proj_run_config(%s, m=%d, %s)" % (_layers.layer_name(layer), m, cfg.as_dict()))
+
+
+def proj_compressed(layer):
+    """Correction slots per row of the layer's 12-bit form, or -1 if it has none."""
+    rc = _lib().proj_compressed(_layers.layer_id(layer))
+    if rc < -1:
+        _check(rc, "proj_compressed")
+    return rc
 
 
 def proj_release(layer):

@@ -22,6 +22,7 @@ SOURCES = [
     "skinny_bf16_nt1.hip",
     "skinny_bf16_nt2.hip",
     "skinny_f32.hip",
+    "skinny_z.hip",
     "tiled_variants.hip",
     "rowdot_variants.hip",
     "wide_variants.hip",

@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int kWave = 64;
 
@@ -39,6 +40,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+
+// 12-bit weights (lossless; the report's round-5 format: the low byte of each
+// BF16 weight kept raw, the sign and a 3-bit code for one of eight exponent
+// values chosen per matrix). A lane's eight weights w0..w7 of an MFMA A
+// fragment take 12 bytes: dword 0 the low bytes of w0..w3, dword 1 those of
+// w4..w7, dword 2 byte i = n(w_i) | n(w_{i+4}) << 4 with n = sign << 3 | code.
+// The code indexes a table of eight high-byte values (BF16 bits 14..8),
+// bytes 0..3 in t0 and 4..7 in t1, so one byte permute maps four codes at
+// once. Returns the eight BF16 weights in the A-operand layout (w_{2j} in
+// the low half of dword j).
+__device__ __forceinline__ u32x4 decode12(u32x3 v, uint32_t t0, uint32_t t1)
+{
+    const uint32_t qa = v.z & 0x0f0f0f0fu;
+    const uint32_t qb = (v.z >> 4) & 0x0f0f0f0fu;
+    const uint32_t ha = __builtin_amdgcn_perm(t1, t0, qa & 0x07070707u) | ((qa << 4) & 0x80808080u);
+    const uint32_t hb = __builtin_amdgcn_perm(t1, t0, qb & 0x07070707u) | ((qb << 4) & 0x80808080u);
+    return u32x4{__builtin_amdgcn_perm(ha, v.x, 0x05010400u), __builtin_amdgcn_perm(ha, v.x, 0x07030602u),
+                 __builtin_amdgcn_perm(hb, v.y, 0x05010400u), __builtin_amdgcn_perm(hb, v.y, 0x07030602u)};
+}
+
+// BF16 bits -> FP32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __builtin_bit_cast(float, bits << 16); }
 
 // Exact three-way split of eight FP32 weights into BF16 parts, w = hi + mid + lo.
 // hi keeps the top 8 significand bits (truncation), mid the next 8 of the

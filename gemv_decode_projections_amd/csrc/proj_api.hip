@@ -2,6 +2,9 @@
 // dispatch and launch. Declarations and the call contract are in proj.h.
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include <hip/hip_ext.h>
 
 #include "../../include/proj.h"
@@ -50,6 +53,11 @@ struct LayerState {
     uint16_t *zrow = nullptr;     // K zero BF16 values: activation rows past m
     void *wrow = nullptr;         // row-major copy of the first wrow_rows rows (row-dot kernel)
     int wrow_rows = 0;
+    // 12-bit form (BF16 layers whose rows need at most kZMaxSlots corrections)
+    uint32_t *wz = nullptr;       // packed 12-bit fragments
+    uint64_t *zexc = nullptr;     // corrections: N rows x zcr slots
+    int zcr = -1;                 // slots per row; -1: no 12-bit form
+    uint32_t zt0 = 0, zt1 = 0;    // exponent table
     int device = -1;
     bool prepared = false;
 };
@@ -72,14 +80,21 @@ int n_eff_of(int layer, int m)
     return kLayers[layer].N;
 }
 
-const SkinnyVariant *find_variant(int nt, int rb, int waves, int spw, int f32w)
+const SkinnyVariant *const kSkinnyParts[4] = {kSkinnyPartBf16Nt1, kSkinnyPartBf16Nt2, kSkinnyPartF32, kSkinnyPartZ};
+
+int skinny_part_count(int p)
 {
-    const SkinnyVariant *parts[3] = {kSkinnyPartBf16Nt1, kSkinnyPartBf16Nt2, kSkinnyPartF32};
-    const int counts[3] = {kSkinnyPartBf16Nt1Count, kSkinnyPartBf16Nt2Count, kSkinnyPartF32Count};
-    for (int p = 0; p < 3; ++p)
-        for (int i = 0; i < counts[p]; ++i) {
-            const SkinnyVariant &v = parts[p][i];
-            if (v.nt == nt && v.rb == rb && v.waves == waves && v.spw == spw && v.f32w == f32w)
+    const int counts[4] = {kSkinnyPartBf16Nt1Count, kSkinnyPartBf16Nt2Count, kSkinnyPartF32Count,
+                           kSkinnyPartZCount};
+    return counts[p];
+}
+
+const SkinnyVariant *find_variant(int nt, int rb, int waves, int spw, int f32w, int z)
+{
+    for (int p = 0; p < 4; ++p)
+        for (int i = 0; i < skinny_part_count(p); ++i) {
+            const SkinnyVariant &v = kSkinnyParts[p][i];
+            if (v.nt == nt && v.rb == rb && v.waves == waves && v.spw == spw && v.f32w == f32w && v.z == z)
                 return &v;
         }
     return nullptr;
@@ -115,7 +130,10 @@ const RowVariant *find_row(int mcap, int r, int kit, int f32w)
     return nullptr;
 }
 
-int skinny_variants() { return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count; }
+int skinny_variants()
+{
+    return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count + kSkinnyPartZCount;
+}
 
 int total_variants() { return skinny_variants() + kTiledVariantCount + kRowVariantCount + kWideVariantCount; }
 
@@ -123,14 +141,11 @@ const SkinnyVariant *variant_at(int i)
 {
     if (i < 0)
         return nullptr;
-    if (i < kSkinnyPartBf16Nt1Count)
-        return &kSkinnyPartBf16Nt1[i];
-    i -= kSkinnyPartBf16Nt1Count;
-    if (i < kSkinnyPartBf16Nt2Count)
-        return &kSkinnyPartBf16Nt2[i];
-    i -= kSkinnyPartBf16Nt2Count;
-    if (i < kSkinnyPartF32Count)
-        return &kSkinnyPartF32[i];
+    for (int p = 0; p < 4; ++p) {
+        if (i < skinny_part_count(p))
+            return &kSkinnyParts[p][i];
+        i -= skinny_part_count(p);
+    }
     return nullptr;
 }
 
@@ -157,7 +172,10 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
     if (c.ksplit < 1)
         return PROJ_ERR_UNSUPPORTED;
     if (c.kind == 0) {
-        const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w);
+        const int z = (c.flags & 4) ? 1 : 0;
+        if (z && st.zcr < 0)
+            return PROJ_ERR_UNSUPPORTED;              // no 12-bit form for this layer
+        const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w, z);
         if (!v)
             return PROJ_ERR_UNSUPPORTED;
         if (c.waves * c.spw * c.ksplit != KS)
@@ -179,8 +197,14 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         L.fn = v->fn;
         L.kind = 0;
         L.grid = (int)grid;
-        L.block = c.waves * kWave;
+        L.block = (c.waves + z) * kWave;
         SkinnyArgs &A = L.sargs;
+        A.wz = st.wz;
+        A.wz_bytes = (uint32_t)((size_t)li.N * li.K * 3 / 2);
+        A.zt0 = st.zt0;
+        A.zt1 = st.zt1;
+        A.zcr = z ? st.zcr : 0;
+        A.zexc = st.zexc;
         A.wp = st.wp;
         A.ws = st.ws;
         A.counters = st.counters;
@@ -303,20 +327,23 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
 proj_config plan_default(int layer, int m)
 {
     struct Entry {
-        int nt, rb, waves, spw, ksplit;
+        int nt, rb, waves, spw, ksplit, z;   // z: read the 12-bit weights when the layer has them
     };
-    // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32.
+    // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32. The 12-bit
+    // form pays where the weight stream dominates (pooler up to 16 tokens,
+    // the full unpooler at 9-16); qkv_gate measured even and o slower (a
+    // short stream, where the correction wave and epilogue pass do not hide).
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {2, 2, 4, 32, 2}},
+        {{1, 1, 8, 32, 1, 0}, {1, 1, 8, 32, 1, 0}, {2, 2, 4, 32, 2, 0}},
         /* o         512 row blocks,  32 k-steps */
-        {{1, 2, 4, 8, 1}, {1, 2, 4, 8, 1}, {2, 2, 4, 8, 1}},
+        {{1, 2, 4, 8, 1, 0}, {1, 2, 4, 8, 1, 0}, {2, 2, 4, 8, 1, 0}},
         /* pooler    256 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1}, {1, 1, 8, 32, 1}, {1, 2, 16, 16, 1}},
+        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {1, 2, 16, 16, 1, 0}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
-        {{1, 1, 8, 16, 1}, {1, 1, 4, 32, 1}, {2, 2, 4, 32, 1}},
+        {{1, 1, 8, 16, 1, 0}, {1, 1, 4, 32, 1, 1}, {2, 2, 4, 32, 1, 0}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
-        {{1, 1, 8, 4, 8}, {1, 1, 16, 2, 8}, {1, 1, 8, 4, 8}},
+        {{1, 1, 8, 4, 8, 0}, {1, 1, 16, 2, 8, 0}, {1, 1, 8, 4, 8, 0}},
     };
     proj_config c{};
     // Few tokens on the router (m <= 8) and the unpooler slice (m <= 4):
@@ -340,6 +367,7 @@ proj_config plan_default(int layer, int m)
         c.waves = e.waves;
         c.spw = e.spw;
         c.ksplit = e.ksplit;
+        c.flags = (e.z && g_layers[layer].zcr >= 0) ? 4 : 0;
         return c;
     }
     // Larger m: the tiled kernel (kind 1) or the wide-tile kernel (kind 3),
@@ -421,6 +449,68 @@ int launch(const Launch &L, const void *x, void *out, hipStream_t stream, hipEve
     return PROJ_OK;
 }
 
+// The 12-bit form of a BF16 layer (format: common.h decode12, repack.h
+// repack_z_kernel). The exponent table is the eight consecutive values of
+// BF16 bits 14..8 that cover the most weights (the report's round-5 rule);
+// every other weight gets a correction slot in its row: k, its own bits w
+// and the bits d that its clamped 12-bit code decodes to. Rows are padded to
+// the largest count with empty slots (k = 0xffff). A layer whose rows need
+// more than kZMaxSlots slots keeps only the BF16 form (zcr = -1).
+int encode_z(const LayerInfo &li, const void *W, LayerState &ns)
+{
+    const size_t n = (size_t)li.N * li.K;
+    std::vector<uint16_t> h(n);
+    hipError_t e = hipMemcpy(h.data(), W, n * 2, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    size_t hist[128] = {0};
+    for (size_t i = 0; i < n; ++i)
+        ++hist[(h[i] >> 8) & 0x7f];
+    int base = 0;
+    size_t best = 0;
+    for (int b = 0; b + 8 <= 128; ++b) {
+        size_t c = 0;
+        for (int j = 0; j < 8; ++j)
+            c += hist[b + j];
+        if (c > best) {
+            best = c;
+            base = b;
+        }
+    }
+    std::vector<std::vector<uint64_t>> rows(li.N);
+    size_t cr = 0;
+    for (int r = 0; r < li.N; ++r) {
+        for (int k = 0; k < li.K; ++k) {
+            const uint32_t w = h[(size_t)r * li.K + k];
+            const int hx = (int)((w >> 8) & 0x7fu);
+            if (hx >= base && hx < base + 8)
+                continue;
+            const uint32_t c = (uint32_t)std::min(std::max(hx - base, 0), 7);
+            const uint32_t d = (w & 0x8000u) | ((uint32_t)(base + (int)c) << 8) | (w & 0xffu);
+            rows[r].push_back((uint64_t)k | ((uint64_t)w << 16) | ((uint64_t)d << 32));
+        }
+        cr = std::max(cr, rows[r].size());
+        if (cr > (size_t)kZMaxSlots)
+            return PROJ_OK;                   // too many corrections: BF16 form only
+    }
+    std::vector<uint64_t> tab((size_t)li.N * std::max<size_t>(cr, 1), 0xffffull);
+    for (int r = 0; r < li.N; ++r)
+        for (size_t j = 0; j < rows[r].size(); ++j)
+            tab[(size_t)r * cr + j] = rows[r][j];
+    if ((e = hipMalloc(reinterpret_cast<void **>(&ns.wz), n * 3 / 2)) != hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void **>(&ns.zexc), tab.size() * 8)) != hipSuccess ||
+        (e = hipMemcpy(ns.zexc, tab.data(), tab.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
+        return hip_fail(e);
+    hipLaunchKernelGGL(repack_z_kernel, dim3(4096), dim3(256), 0, nullptr, static_cast<const uint16_t *>(W), ns.wz,
+                       li.N, li.K, base);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return hip_fail(e);
+    ns.zcr = (int)cr;
+    ns.zt0 = (uint32_t)base | (uint32_t)(base + 1) << 8 | (uint32_t)(base + 2) << 16 | (uint32_t)(base + 3) << 24;
+    ns.zt1 = (uint32_t)(base + 4) | (uint32_t)(base + 5) << 8 | (uint32_t)(base + 6) << 16 | (uint32_t)(base + 7) << 24;
+    return PROJ_OK;
+}
+
 void free_layer(LayerState &st)
 {
     if (st.wp)
@@ -433,6 +523,10 @@ void free_layer(LayerState &st)
         (void)hipFree(st.zrow);
     if (st.wrow)
         (void)hipFree(st.wrow);
+    if (st.wz)
+        (void)hipFree(st.wz);
+    if (st.zexc)
+        (void)hipFree(st.zexc);
     st = LayerState{};
 }
 
@@ -481,9 +575,15 @@ int proj_prepare(int layer, const void *W)
     }
     const int threads = 256;
     const int blocks = 4096;
-    if (li.w_bytes == 2)
+    if (li.w_bytes == 2) {
         hipLaunchKernelGGL(repack_bf16_kernel, dim3(blocks), dim3(threads), 0, nullptr,
                            static_cast<const uint16_t *>(W), static_cast<u32x4 *>(ns.wp), li.N, li.K);
+        const int rc = encode_z(li, W, ns);
+        if (rc) {
+            free_layer(ns);
+            return rc;
+        }
+    }
     else
         hipLaunchKernelGGL(repack_f32_kernel, dim3(blocks), dim3(threads), 0, nullptr,
                            static_cast<const float *>(W), static_cast<u32x4 *>(ns.wp), li.N, li.K);
@@ -673,10 +773,21 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
         c.waves = v->waves;
         c.spw = v->spw;
         c.ksplit = 1;
-        c.block = v->waves * kWave;
+        c.flags = v->z ? 4 : 0;
+        c.block = (v->waves + v->z) * kWave;
         *cfg = c;
     }
     return PROJ_OK;
+}
+
+int proj_compressed(int layer)
+{
+    if (check_layer(layer))
+        return PROJ_ERR_LAYER;
+    const LayerState &st = g_layers[layer];
+    if (!st.prepared)
+        return PROJ_ERR_NOT_PREPARED;
+    return st.zcr < 0 ? -1 : st.zcr;
 }
 
 }  // extern "C"

@@ -28,7 +28,19 @@
 //     tile's counter for the next launch.
 //   * FP32 router weights are split exactly into three BF16 parts in
 //     registers (common.h) and accumulated by three MFMAs in FP32.
+//   * Z: weights read in the 12-bit lossless form (common.h, decode12; the
+//     report's round 5 found 25 % fewer bytes worth ~20 % of a decode GEMV):
+//     12 bytes per lane per fragment (one dwordx3 load, a wave's 768 bytes
+//     contiguous), decoded with byte permutes right before the MFMA. Weights
+//     outside the exponent table are corrected from a per-row list of
+//     (k, w, d) with d the value the 12-bit form decodes to: one extra wave
+//     loads the workgroup's list and gathers the activations it needs while
+//     the other waves stream, and the epilogue applies (acc - d*x) + w*x in
+//     list order (both products exact in FP32, so a one-hot activation row
+//     returns the original weight bit for bit).
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -47,11 +59,21 @@ struct SkinnyArgs {
     int n_tt;                // token tiles (ceil(m / (16 * NT)))
     int ksplit;              // workgroups per tile along K
     int xcd_remap;           // 1: spread consecutive logical tiles on one XCD
+    // 12-bit weights (Z variants only)
+    const uint32_t *wz;      // packed 12-bit fragments
+    uint32_t wz_bytes;
+    uint32_t zt0, zt1;       // exponent table (high bytes), codes 0..3 and 4..7
+    int zcr;                 // correction slots per row (0: none)
+    const uint64_t *zexc;    // per row zcr slots: k | w << 16 | d << 32 (k = 0xffff: empty)
 };
 
-template <int NT, int RB, int WAVES, int SPW, bool F32W>
-__global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
+constexpr int kZMaxSlots = 8;    // correction slots per row a 12-bit layer may use
+
+template <int NT, int RB, int WAVES, int SPW, bool F32W, bool Z = false>
+__global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(SkinnyArgs a)
 {
+    static_assert(!(Z && F32W), "12-bit weights are BF16 only");
+    static_assert(!Z || (WAVES > 1 && NT == 1), "12-bit variants: several waves, one 16-token sub-tile");
     constexpr int U = SPW < 4 ? SPW : 4;             // k-steps per pipeline stage
     static_assert(SPW % U == 0, "SPW must be a multiple of the stage size");
     constexpr int NSTAGE = SPW / U;
@@ -113,7 +135,11 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
             acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 wa[2][U][RB][AW];
+    u32x3 wq[2][U][RB];
     u32x4 xb[2][U][NT];
+    // Buffer descriptor over the 12-bit weights (built but unused when !Z).
+    const __amdgpu_buffer_rsrc_t wzr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(a.wz), (short)0, (int)a.wz_bytes, 0x00020000);
 
     // Plain (cached) loads: measured faster than non-temporal ones for the
     // weight stream on this part.
@@ -123,10 +149,15 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
             const int step = step0 + ((local + u + rot) & (SPW - 1));
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                const u32x4 *f = wbase + ((size_t)(rb0 + r) * KS + step) * FRAG_U4 + lane;
+                if constexpr (Z) {
+                    wq[buf][u][r] = __builtin_amdgcn_raw_buffer_load_b96(
+                        wzr, (uint32_t)((((rb0 + r) * KS + step) * kWave + lane) * 12), 0, 0);
+                } else {
+                    const u32x4 *f = wbase + ((size_t)(rb0 + r) * KS + step) * FRAG_U4 + lane;
 #pragma unroll
-                for (int h = 0; h < AW; ++h)
-                    wa[buf][u][r][h] = f[h * kWave];
+                    for (int h = 0; h < AW; ++h)
+                        wa[buf][u][r][h] = f[h * kWave];
+                }
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -157,26 +188,96 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
                         acc[r][t] = mfma16x16x32(lo, xb[buf][u][t], acc[r][t]);
                     }
                 } else {
+                    const u32x4 wf = Z ? decode12(wq[buf][u][r], a.zt0, a.zt1) : wa[buf][u][r][0];
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
-                        acc[r][t] = mfma16x16x32(wa[buf][u][r][0], xb[buf][u][t], acc[r][t]);
+                        acc[r][t] = mfma16x16x32(wf, xb[buf][u][t], acc[r][t]);
                 }
             }
         }
     };
 
-    load_stage(0, 0);
-    if constexpr (NSTAGE > 1)
-        load_stage(1, U);
+    // 12-bit corrections: this workgroup's rows' slots (zcr per row; row r's
+    // slot c at r * kZMaxSlots + c here), each with its weight pair and the
+    // activations of the tile's tokens at k, and per row a byte mask of the
+    // slots that are live in this split (entry present, k in its range).
+    constexpr int ZSLOTS = Z ? 16 * RB * kZMaxSlots : 1;
+    constexpr int ZTOK = 16 * NT;
+    __shared__ float zw[ZSLOTS], zd[ZSLOTS], zx[ZSLOTS][Z ? ZTOK : 1];
+    __shared__ __attribute__((aligned(8))) uint8_t zlive[ZSLOTS];
+    const bool exc_wave = Z && wave == WAVES;
+
+    if (exc_wave) {
+        if constexpr (Z) {
+          if (a.zcr > 0) {
+            // Every load is issued before any is used: slot entries first,
+            // then the activation gathers (one token when the tile holds
+            // one), so the wave pays two memory round trips while the others
+            // stream weights.
+            constexpr int EPL = ZSLOTS / kWave;       // slots per lane (at the maximum)
+            const int nslot = 16 * RB * a.zcr;
+            const uint64_t *src = a.zexc + (size_t)rb0 * 16 * a.zcr;
+            const int k_lo = (ks * WAVES) * SPW * kStepK, k_hi = k_lo + WAVES * SPW * kStepK;
+            const int ntok = min(a.m - tt * ZTOK, ZTOK);   // live tokens of this tile
+            uint64_t ent[EPL];
 #pragma unroll
-    for (int s = 0; s < NSTAGE; s += 2) {
-        compute_stage(0);
-        if (s + 2 < NSTAGE)
-            load_stage(0, (s + 2) * U);
-        if (s + 1 < NSTAGE) {
-            compute_stage(1);
-            if (s + 3 < NSTAGE)
-                load_stage(1, (s + 3) * U);
+            for (int i = 0; i < EPL; ++i)
+                ent[i] = src[min(lane + kWave * i, nslot - 1)];
+            uint32_t xv[EPL][ZTOK];
+            auto gather = [&](auto ntok_c) {
+                constexpr int NTK = decltype(ntok_c)::value;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) {
+                    const int k = (int)(ent[i] & 0xffffu);
+                    const int kk = k < a.K ? k : 0;
+#pragma unroll
+                    for (int t = 0; t < NTK; ++t)
+                        xv[i][t] = a.x[(size_t)min(tt * ZTOK + t, a.m - 1) * a.K + kk];
+                }
+            };
+            if (ntok == 1)
+                gather(std::integral_constant<int, 1>{});
+            else
+                gather(std::integral_constant<int, ZTOK>{});
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int j = lane + kWave * i;
+                const int k = (int)(ent[i] & 0xffffu);
+                const bool live = j < nslot && k >= k_lo && k < k_hi;
+                const int r = j / a.zcr, c = j - (j / a.zcr) * a.zcr;
+                const int sl = r * kZMaxSlots + c;
+                if (j < nslot) {
+                    zlive[sl] = live ? 1 : 0;
+                    zw[sl] = bf16_to_f32((uint32_t)(ent[i] >> 16) & 0xffffu);
+                    zd[sl] = bf16_to_f32((uint32_t)(ent[i] >> 32) & 0xffffu);
+#pragma unroll
+                    for (int t = 0; t < ZTOK; ++t)
+                        zx[sl][t] = t < ntok ? bf16_to_f32(xv[i][ntok == 1 ? 0 : t]) : 0.f;
+                }
+            }
+            // Slots past zcr in each row stay dead.
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int sl = lane + kWave * i;
+                if ((sl % kZMaxSlots) >= a.zcr)
+                    zlive[sl] = 0;
+            }
+          }
+        }
+    } else {
+        load_stage(0, 0);
+        if constexpr (NSTAGE > 1)
+            load_stage(1, U);
+#pragma unroll
+        for (int s = 0; s < NSTAGE; s += 2) {
+            compute_stage(0);
+            if (s + 2 < NSTAGE)
+                load_stage(0, (s + 2) * U);
+            if (s + 1 < NSTAGE) {
+                compute_stage(1);
+                if (s + 3 < NSTAGE)
+                    load_stage(1, (s + 3) * U);
+            }
         }
     }
 
@@ -186,19 +287,66 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
     __shared__ f32x4 red[WAVES > 1 ? WAVES : 1][TILES][kWave];
     __shared__ int s_last;
     if constexpr (WAVES > 1) {
+        if (!exc_wave) {
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+            for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                red[wave][r * NT + t][lane] = acc[r][t];
+                for (int t = 0; t < NT; ++t)
+                    red[wave][r * NT + t][lane] = acc[r][t];
+        }
         __syncthreads();
     }
 
     const int tile = rt * a.n_tt + tt;
     f32x4 *wsp = a.ws + ((size_t)tile * a.ksplit) * ELEMS;
 
+    // 12-bit corrections, applied once per (row, token) by its own thread
+    // (spread over the whole workgroup, so each thread's chain of dependent
+    // LDS reads is one row long): zfin = sum of the waves' partials in wave
+    // order, then for each live slot of the row in slot order
+    // v = (v - d*x) + w*x.
+    constexpr int ZROWS = 16 * RB;
+    __shared__ float zfin[Z ? ZROWS : 1][Z ? ZTOK : 1];
+    if constexpr (Z && WAVES > 1) {
+        if (a.zcr > 0) {
+            for (int p = threadIdx.x; p < ZROWS * ZTOK; p += (WAVES + 1) * kWave) {
+                const int row = p / ZTOK, tl = p % ZTOK;
+                const int r = row / kRowsPerBlock, rr = row % kRowsPerBlock;
+                const int j = r * NT + tl / 16;
+                const int ln = 16 * (rr / 4) + tl % 16;
+                float v = reinterpret_cast<const float *>(&red[0][j][ln])[rr % 4];
+#pragma unroll
+                for (int w = 1; w < WAVES; ++w)
+                    v += reinterpret_cast<const float *>(&red[w][j][ln])[rr % 4];
+                if (tt * ZTOK + tl < a.m) {
+                    uint64_t live = *reinterpret_cast<const uint64_t *>(&zlive[row * kZMaxSlots]);
+                    while (live) {
+                        const int c = __builtin_ctzll(live) / 8;
+                        live &= live - 1;
+                        const int sl = row * kZMaxSlots + c;
+                        const float xv = zx[sl][tl];
+                        v = (v - zd[sl] * xv) + zw[sl] * xv;
+                    }
+                }
+                zfin[row][tl] = v;
+            }
+            __syncthreads();
+        }
+    }
+
+    // Sum of the waves' partials for element e (with the 12-bit corrections
+    // when there are any).
     auto wave_sum = [&](int e) -> f32x4 {
         if constexpr (WAVES > 1) {
+            if constexpr (Z) {
+                if (a.zcr > 0) {
+                    const int j = e / kWave, ln = e % kWave;
+                    const int r = j / NT, t = j % NT;
+                    const int tl = t * 16 + (ln % 16);
+                    const int row0 = r * kRowsPerBlock + 4 * (ln / 16);
+                    return f32x4{zfin[row0][tl], zfin[row0 + 1][tl], zfin[row0 + 2][tl], zfin[row0 + 3][tl]};
+                }
+            }
             f32x4 v = red[0][e / kWave][e % kWave];
 #pragma unroll
             for (int w = 1; w < WAVES; ++w)
@@ -227,9 +375,10 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
     };
 
     // With WAVES == 1 only the owning lane may read its accumulators.
+    constexpr int NTHR = (WAVES + (Z ? 1 : 0)) * kWave;
     if (a.ksplit == 1) {
         if constexpr (WAVES > 1) {
-            for (int e = threadIdx.x; e < ELEMS; e += WAVES * kWave)
+            for (int e = threadIdx.x; e < ELEMS; e += NTHR)
                 store_out(e, wave_sum(e));
         } else {
 #pragma unroll
@@ -249,7 +398,6 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
     // Values move as 8-byte words (an f32x4 is two words, low element first).
     // The last workgroup gathers WAVES splits per round, one per wave, with
     // all of a wave's loads in flight at once, and sums them through LDS.
-    constexpr int NTHR = WAVES * kWave;
     constexpr int EPT = (ELEMS + NTHR - 1) / NTHR;  // output elements per thread
     uint64_t *wsw = reinterpret_cast<uint64_t *>(wsp);
     for (int e = threadIdx.x; e < ELEMS; e += NTHR) {
@@ -286,11 +434,13 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(SkinnyArgs a)
                 wd[j][h] = __hip_atomic_load(src + (j * kWave + lane) * 2 + h, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();                             // earlier readers of red are done
+        if (!exc_wave) {
 #pragma unroll
-        for (int j = 0; j < TILES; ++j) {
-            const u32x4 u = {(uint32_t)wd[j][0], (uint32_t)(wd[j][0] >> 32), (uint32_t)wd[j][1],
-                             (uint32_t)(wd[j][1] >> 32)};
-            red[wave][j][lane] = __builtin_bit_cast(f32x4, u);
+            for (int j = 0; j < TILES; ++j) {
+                const u32x4 u = {(uint32_t)wd[j][0], (uint32_t)(wd[j][0] >> 32), (uint32_t)wd[j][1],
+                                 (uint32_t)(wd[j][1] >> 32)};
+                red[wave][j][lane] = __builtin_bit_cast(f32x4, u);
+            }
         }
         __syncthreads();
         const int nw = min(WAVES, a.ksplit - s0);

@@ -12,6 +12,7 @@ struct SkinnyVariant {
     int spw;
     int f32w;
     const void *fn;   // __global__ void (SkinnyArgs)
+    int z;            // 1: reads the 12-bit weights (one extra wave per workgroup)
 };
 
 // Tiled (large-m) kernel variants: BMB x BNB blocks of 16 per workgroup, WR waves
@@ -52,6 +53,8 @@ extern const SkinnyVariant kSkinnyPartBf16Nt2[];
 extern const int kSkinnyPartBf16Nt2Count;
 extern const SkinnyVariant kSkinnyPartF32[];
 extern const int kSkinnyPartF32Count;
+extern const SkinnyVariant kSkinnyPartZ[];
+extern const int kSkinnyPartZCount;
 extern const TiledVariant kTiledVariants[];
 extern const int kTiledVariantCount;
 extern const WideVariant kWideVariants[];

@@ -115,6 +115,19 @@ int proj_out_cols(int layer, int m);
  */
 int proj_layer_dims(int layer, int *N, int *K, int *w_elem_bytes, int *out_elem_bytes);
 
+/*
+ * proj_compressed - whether prepare also stored the layer's weights in the
+ * 12-bit lossless form (report "Muse Spark Open Kernel Challenge -
+ * muse_bf16_proj", round 5: each BF16 weight keeps its low byte and gets a
+ * sign plus a 3-bit code for one of eight exponent values chosen per
+ * matrix; weights outside those eight are restored exactly from a per-row
+ * correction list). Returns the correction slots per row (0..8) when it
+ * did, -1 when the layer is FP32 (router) or some row would need more than 8
+ * corrections (then only the BF16 form exists), PROJ_ERR_LAYER or
+ * PROJ_ERR_NOT_PREPARED otherwise. Host-only; no GPU call.
+ */
+int proj_compressed(int layer);
+
 /* proj_release - free a layer's packed weights and workspace; idempotent. */
 int proj_release(int layer);
 
@@ -151,6 +164,9 @@ int proj_last_hip_error(void);
  *   flags     bit 0 set: workgroup i keeps tile i. Clear (default): when the
  *             grid is a multiple of 8, consecutive tiles are grouped on one
  *             XCD (workgroups are dealt to the 8 XCDs round-robin).
+ *             bit 2 set (kind 0 with nt 1 and waves > 1): read the 12-bit
+ *             weights (needs proj_compressed(layer) >= 0); the workgroup gets
+ *             one more wave, which gathers the correction terms.
  * proj_plan fills the configuration proj_run would use; proj_run_config runs
  * an explicit one and returns PROJ_ERR_UNSUPPORTED if it is not compiled or
  * does not tile the layer.
@@ -162,7 +178,7 @@ typedef struct {
     int waves;
     int spw;
     int ksplit;
-    int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping) */
+    int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping); bit 2: 12-bit weights */
     int grid;      /* filled by proj_plan: workgroups launched */
     int block;     /* filled by proj_plan: threads per workgroup */
 } proj_config;

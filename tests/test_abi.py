@@ -46,6 +46,11 @@ def test_layer_table_matches_python_side(lib):
             assert binding.proj_out_cols(name, m) == layers.n_eff(name, m)
 
 
+def test_compressed_query_without_gpu(lib):
+    assert lib.proj_compressed(9) == -1          # PROJ_ERR_LAYER
+    assert lib.proj_compressed(4) == -5          # router not prepared here
+
+
 def test_host_side_errors_without_gpu(lib):
     vp = ctypes.c_void_p
     assert lib.proj_out_cols(5, 1) == -1
@@ -73,7 +78,7 @@ def test_dispatch_plans_tile_every_layer(lib):
         for m in list(range(1, 41)) + [64, 100, 127, 128, 129, 130, 200, 256, 512, 1000, 4096]:
             cfg = binding.proj_plan(name, m)
             ne = layers.n_eff(name, m)
-            assert cfg.block == 64 * cfg.waves
+            assert cfg.block == 64 * (cfg.waves + (1 if cfg.flags & 4 else 0))
             if cfg.kind == 2:
                 # whole rows per workgroup: router and the unpooler slice at m <= 8
                 assert name in ("router", "unpooler") and m <= cfg.nt <= 8 and cfg.ksplit == 1
@@ -100,7 +105,7 @@ def test_variant_registry(lib):
     seen = set()
     for i in range(nv):
         f32, cfg = binding.proj_variant(i)
-        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw)
+        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags & 4)
         assert key not in seen
         seen.add(key)
     with pytest.raises(binding.ProjError):

@@ -131,7 +131,7 @@ def _variant_cases():
             if cfg.kind == 0:
                 if ks % (cfg.waves * cfg.spw) == 0:
                     split = ks // (cfg.waves * cfg.spw)
-                    cases.append((layer, 0, cfg.nt, cfg.rb, cfg.waves, cfg.spw, split, 0))
+                    cases.append((layer, 0, cfg.nt, cfg.rb, cfg.waves, cfg.spw, split, cfg.flags))
                     break
             elif cfg.kind == 1 and n % (16 * cfg.rb) == 0:
                 cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 1, 0))
@@ -239,6 +239,85 @@ def test_graph_replay_fresh_inputs(layer, m):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32),
                        prev_bits.view(torch.int16) if out.dtype == torch.bfloat16 else prev_bits.view(torch.int32))
+
+
+def _exception_columns(w, limit=3):
+    """Columns holding weights outside the 12-bit exponent table: the eight
+    consecutive values of BF16 bits 14..8 that cover the most weights (the
+    report's round-5 rule, recomputed here from the host weights)."""
+    h = (w >> 8) & 0x7F
+    hist = np.bincount(h.ravel(), minlength=128)
+    base = int(np.argmax([hist[b:b + 8].sum() for b in range(121)]))
+    exc = (h < base) | (h > base + 7)
+    cols = np.nonzero(exc.any(axis=0))[0]
+    return [int(c) for c in cols[:limit]], exc
+
+
+def test_layers_keep_a_12bit_form():
+    prepared(0)
+    for layer in ("qkv_gate", "o", "pooler", "unpooler"):
+        assert 0 <= binding.proj_compressed(layer) <= 8, layer
+    assert binding.proj_compressed("router") == -1
+
+
+@pytest.mark.parametrize("layer", ["qkv_gate", "o", "pooler", "unpooler"])
+@pytest.mark.parametrize("m", [1, 5, 16])
+def test_12bit_exception_columns_bit_exact(layer, m):
+    """A one-hot activation row on a column holding out-of-table weights returns
+    that weight column times the scale bit for bit through the 12-bit path
+    (report round 5: the corrections restore the original weights exactly);
+    the other rows are ordinary inputs checked against the oracle."""
+    p = prepared(0)
+    w = p.w[layer]
+    cols, exc = _exception_columns(w)
+    assert cols, "weights without any out-of-table value"
+    n_eff = binding.proj_out_cols(layer, m)
+    cfg = binding.ProjConfig.make(kind=0, nt=1, rb=1, waves=8, spw=SHAPES[layer][1] // 256, ksplit=1, flags=4)
+    for k in cols:
+        xs = make_x(layer, m, seed=1200 + k)
+        bits = xs.bits.copy()
+        bits[0, :] = 0
+        bits[0, k] = bf16_bits_from_f32(np.array([2.0 ** -3], dtype=np.float32))[0]
+        xs.bits = bits
+        say("12-bit exception column", layer, "m=%d" % m, "k=%d" % k, "rows with exceptions", int(exc[:n_eff, k].sum()))
+        got = run_layer(layer, bits, cfg=cfg)
+        want = f32_from_bf16_bits(w[:n_eff, k]).astype(np.float64) * 2.0 ** -3
+        assert np.array_equal(got[0], want)
+        if m > 1:
+            xs.probes = [pr for pr in xs.probes if pr[0] != 0]
+            r = compare(layer, got[1:], w, _RowsView(xs, 1))
+            assert r.ok, r
+
+
+class _RowsView:
+    """x rows [start:] of a seeded input, with its probe rows renumbered."""
+
+    def __init__(self, xs, start):
+        self.bits = xs.bits[start:]
+        self.probes = [(r - start, k, e) for (r, k, e) in xs.probes if r >= start]
+        self.probe_rows = [r for (r, _, _) in self.probes]
+
+
+def test_12bit_form_skipped_when_a_row_needs_too_many_corrections():
+    """Weights with more out-of-table values in one row than the correction
+    slots hold: prepare keeps only the BF16 form, the dispatch does not ask
+    for 12-bit weights, and results stay exact."""
+    _dirty()
+    w = make_weight("pooler", 0).copy()
+    w[7, 100:140:4] = 0                      # ten exact zeros in row 7: all outside the table
+    binding.proj_prepare("pooler", to_device_weight("pooler", w))
+    assert binding.proj_compressed("pooler") == -1
+    assert binding.proj_plan("pooler", 1).flags & 4 == 0
+    with pytest.raises(binding.ProjError):
+        binding.proj_run_config("pooler", to_device_x(make_x("pooler", 1, seed=5).bits), 1,
+                                binding.new_out("pooler", 1),
+                                binding.ProjConfig.make(kind=0, nt=1, rb=1, waves=8, spw=32, ksplit=1, flags=4))
+    for m in (1, 16):
+        xs = make_x("pooler", m, seed=1300 + m)
+        got = run_layer("pooler", xs.bits)
+        r = compare("pooler", got, w, xs)
+        assert r.ok, r
+    _dirty()
 
 
 def test_bf16_output_rounding_is_nearest_even():
