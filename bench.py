@@ -219,8 +219,9 @@ def traffic_for(layer, m, kernel=None):
 def kernel_name(cfg, f32w):
     """Template name of the kernel a configuration launches (as profilers print it)."""
     f = "true" if f32w else "false"
-    if cfg.kind == 0:
-        return "skinny_kernel<%d, %d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.waves, cfg.spw, f)
+    if cfg.kind == 0:   # last argument: 12-bit weights
+        return "skinny_kernel<%d, %d, %d, %d, %s, %s>" % (cfg.nt, cfg.rb, cfg.waves, cfg.spw, f,
+                                                          "true" if cfg.flags & 4 else "false")
     if cfg.kind == 1:   # <rows per wave, token blocks, waves, k-steps per super-step, depth, fp32>
         return "tiled_kernel<%d, %d, %d, %d, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.waves,
                                                          min(4, cfg.spw // 2), cfg.spw, f)
@@ -397,6 +398,7 @@ def main():
         sys.exit("bench.py needs a GPU")
     from gemv_decode_projections_amd import roofline as rf
     from gemv_decode_projections_amd import binding as B
+    from gemv_decode_projections_amd import layers as layers_mod
 
     b = Bench()
     layers = b.LAYERS
@@ -466,8 +468,16 @@ def main():
     achieved = dom_bytes / dom_avg / 1e3  # GB/s
     cfg = B.proj_plan(dom, 1)
     kname = kernel_name(cfg, dom == "router")
+    # With 12-bit weights the kernel reads 3/4 of the BF16 weight bytes plus
+    # one correction table; "achieved" still counts the BF16 bytes the
+    # operation is defined on, and stored_bytes says what is actually read.
+    stored = dom_bytes
+    if cfg.kind == 0 and cfg.flags & 4:
+        n, k, _, _ = layers_mod.DIMS[dom]
+        stored = dom_bytes - rf.weight_bytes(dom, 1) // 4 + n * B.proj_compressed(dom) * 8
     roof = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "stored_bytes": stored, "weights": "12-bit lossless" if stored != dom_bytes else "bf16" if dom != "router" else "fp32",
         "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dom, 1, kname),
         "kernel": kname, "layer": dom, "algorithmic_bytes": dom_bytes, "avg_us": round(dom_avg, 3),
         "measured_read_floor_us": round(floor[dom], 3),

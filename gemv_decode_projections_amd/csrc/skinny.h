@@ -203,7 +203,8 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     // slots that are live in this split (entry present, k in its range).
     constexpr int ZSLOTS = Z ? 16 * RB * kZMaxSlots : 1;
     constexpr int ZTOK = 16 * NT;
-    __shared__ float zw[ZSLOTS], zd[ZSLOTS], zx[ZSLOTS][Z ? ZTOK : 1];
+    __shared__ __attribute__((aligned(16))) float zw[ZSLOTS], zd[ZSLOTS];
+    __shared__ float zx[ZSLOTS][Z ? ZTOK : 1];
     __shared__ __attribute__((aligned(8))) uint8_t zlive[ZSLOTS];
     const bool exc_wave = Z && wave == WAVES;
 
@@ -319,13 +320,25 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
                 for (int w = 1; w < WAVES; ++w)
                     v += reinterpret_cast<const float *>(&red[w][j][ln])[rr % 4];
                 if (tt * ZTOK + tl < a.m) {
-                    uint64_t live = *reinterpret_cast<const uint64_t *>(&zlive[row * kZMaxSlots]);
-                    while (live) {
-                        const int c = __builtin_ctzll(live) / 8;
-                        live &= live - 1;
-                        const int sl = row * kZMaxSlots + c;
-                        const float xv = zx[sl][tl];
-                        v = (v - zd[sl] * xv) + zw[sl] * xv;
+                    // All of the row's slots are read at once and the dead
+                    // ones skipped by a select, so the reads overlap instead
+                    // of forming a chain one slot long each.
+                    const int s0 = row * kZMaxSlots;
+                    const uint64_t live = *reinterpret_cast<const uint64_t *>(&zlive[s0]);
+                    const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&zd[s0]);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&zd[s0 + 4]);
+                    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&zw[s0]);
+                    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&zw[s0 + 4]);
+                    float xs[kZMaxSlots];
+#pragma unroll
+                    for (int c = 0; c < kZMaxSlots; ++c)
+                        xs[c] = zx[s0 + c][tl];
+#pragma unroll
+                    for (int c = 0; c < kZMaxSlots; ++c) {
+                        const float d = c < 4 ? d0[c % 4] : d1[c % 4];
+                        const float w = c < 4 ? w0[c % 4] : w1[c % 4];
+                        const float u = (v - d * xs[c]) + w * xs[c];
+                        v = ((live >> (8 * c)) & 1u) ? u : v;
                     }
                 }
                 zfin[row][tl] = v;
