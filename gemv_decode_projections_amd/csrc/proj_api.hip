@@ -330,18 +330,20 @@ proj_config plan_default(int layer, int m)
         int nt, rb, waves, spw, ksplit, z;   // z: read the 12-bit weights when the layer has them
     };
     // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32. The 12-bit
-    // form pays where the weight stream dominates (pooler up to 16 tokens,
-    // the full unpooler at 9-16); qkv_gate measured even and o slower (a
-    // short stream, where the correction wave and epilogue pass do not hide).
+    // form pays where the weight stream is long and one pass over it covers
+    // the tokens (qkv_gate and pooler up to 16 tokens, the full unpooler at
+    // 9-16); o measured slower (a short stream, where the correction wave
+    // and epilogue pass do not hide), and past 16 tokens the BF16 kernels'
+    // wider workgroups win.
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 0}, {1, 1, 8, 32, 1, 0}, {2, 2, 4, 32, 2, 0}},
+        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {2, 2, 4, 32, 2, 0}},
         /* o         512 row blocks,  32 k-steps */
         {{1, 2, 4, 8, 1, 0}, {1, 2, 4, 8, 1, 0}, {2, 2, 4, 8, 1, 0}},
         /* pooler    256 row blocks, 256 k-steps */
         {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {1, 2, 16, 16, 1, 0}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
-        {{1, 1, 8, 16, 1, 0}, {1, 1, 4, 32, 1, 1}, {2, 2, 4, 32, 1, 0}},
+        {{1, 1, 8, 16, 1, 0}, {1, 2, 8, 16, 1, 1}, {2, 2, 4, 32, 1, 0}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
         {{1, 1, 8, 4, 8, 0}, {1, 1, 16, 2, 8, 0}, {1, 1, 8, 4, 8, 0}},
     };
@@ -370,6 +372,21 @@ proj_config plan_default(int layer, int m)
         c.flags = (e.z && g_layers[layer].zcr >= 0) ? 4 : 0;
         return c;
     }
+    // The router past 32 tokens stays on the skinny kernel: with 16 row
+    // blocks the tiled kernels' 64-row tiles leave most compute units idle
+    // or need deep K splits (measured 12-15 us against 8-13.5 here). Two
+    // 16-token blocks per workgroup from 65 tokens, two row blocks past 256.
+    if (layer == PROJ_ROUTER) {
+        static const Entry rtable[4] = {
+            {1, 1, 16, 4, 4, 0}, {2, 1, 16, 4, 4, 0}, {2, 1, 4, 16, 4, 0}, {2, 2, 4, 16, 4, 0}};
+        const Entry &e = rtable[m <= 64 ? 0 : m <= 128 ? 1 : m <= 256 ? 2 : 3];
+        c.nt = e.nt;
+        c.rb = e.rb;
+        c.waves = e.waves;
+        c.spw = e.spw;
+        c.ksplit = e.ksplit;
+        return c;
+    }
     // Larger m: the tiled kernel (kind 1) or the wide-tile kernel (kind 3),
     // picked per layer from measured cold-cache sweeps. Buckets: m <= 64,
     // m <= 128, larger. Entries: kind, 16-row blocks per tile (rb), 16-token
@@ -379,12 +396,11 @@ proj_config plan_default(int layer, int m)
     struct TEntry {
         int kind, rb, nt, depth, ksplit;
     };
-    static const TEntry ttable[PROJ_NUM_LAYERS][3] = {
+    static const TEntry ttable[PROJ_ROUTER][3] = {   // the four BF16 layers
         /* qkv_gate */ {{3, 4, 2, 8, 3}, {3, 4, 4, 8, 3}, {3, 8, 4, 8, 3}},
         /* o        */ {{1, 4, 2, 8, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 4, 1}},
         /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 8, 2}},
         /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 8, 1}},
-        /* router   */ {{1, 4, 2, 8, 16}, {1, 4, 2, 4, 8}, {1, 4, 2, 4, 8}},
     };
     const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : 2)];
     const int ne = n_eff_of(layer, m);

@@ -73,7 +73,7 @@ template <int NT, int RB, int WAVES, int SPW, bool F32W, bool Z = false>
 __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(SkinnyArgs a)
 {
     static_assert(!(Z && F32W), "12-bit weights are BF16 only");
-    static_assert(!Z || (WAVES > 1 && NT == 1), "12-bit variants: several waves, one 16-token sub-tile");
+    static_assert(!Z || WAVES > 1, "12-bit variants need a separate wave for the corrections");
     constexpr int U = SPW < 4 ? SPW : 4;             // k-steps per pipeline stage
     static_assert(SPW % U == 0, "SPW must be a multiple of the stage size");
     constexpr int NSTAGE = SPW / U;
@@ -206,15 +206,16 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     __shared__ __attribute__((aligned(16))) float zw[ZSLOTS], zd[ZSLOTS];
     __shared__ float zx[ZSLOTS][Z ? ZTOK : 1];
     __shared__ __attribute__((aligned(8))) uint8_t zlive[ZSLOTS];
+    __shared__ uint32_t zlist[ZSLOTS];               // live slots: slot | k << 16
     const bool exc_wave = Z && wave == WAVES;
 
     if (exc_wave) {
         if constexpr (Z) {
           if (a.zcr > 0) {
-            // Every load is issued before any is used: slot entries first,
-            // then the activation gathers (one token when the tile holds
-            // one), so the wave pays two memory round trips while the others
-            // stream weights.
+            // The slot entries are loaded at once; the live ones (about one
+            // per row) are packed into a list, and the activations are
+            // gathered for (live slot, token) pairs only, a batch of loads
+            // per lane in flight at a time.
             constexpr int EPL = ZSLOTS / kWave;       // slots per lane (at the maximum)
             const int nslot = 16 * RB * a.zcr;
             const uint64_t *src = a.zexc + (size_t)rb0 * 16 * a.zcr;
@@ -224,22 +225,7 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
                 ent[i] = src[min(lane + kWave * i, nslot - 1)];
-            uint32_t xv[EPL][ZTOK];
-            auto gather = [&](auto ntok_c) {
-                constexpr int NTK = decltype(ntok_c)::value;
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) {
-                    const int k = (int)(ent[i] & 0xffffu);
-                    const int kk = k < a.K ? k : 0;
-#pragma unroll
-                    for (int t = 0; t < NTK; ++t)
-                        xv[i][t] = a.x[(size_t)min(tt * ZTOK + t, a.m - 1) * a.K + kk];
-                }
-            };
-            if (ntok == 1)
-                gather(std::integral_constant<int, 1>{});
-            else
-                gather(std::integral_constant<int, ZTOK>{});
+            int nlive = 0;
 #pragma unroll
             for (int i = 0; i < EPL; ++i) {
                 const int j = lane + kWave * i;
@@ -251,10 +237,11 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
                     zlive[sl] = live ? 1 : 0;
                     zw[sl] = bf16_to_f32((uint32_t)(ent[i] >> 16) & 0xffffu);
                     zd[sl] = bf16_to_f32((uint32_t)(ent[i] >> 32) & 0xffffu);
-#pragma unroll
-                    for (int t = 0; t < ZTOK; ++t)
-                        zx[sl][t] = t < ntok ? bf16_to_f32(xv[i][ntok == 1 ? 0 : t]) : 0.f;
                 }
+                const uint64_t mask = __ballot(live);
+                if (live)
+                    zlist[nlive + __popcll(mask & ((1ull << lane) - 1ull))] = (uint32_t)sl | ((uint32_t)k << 16);
+                nlive += __popcll(mask);
             }
             // Slots past zcr in each row stay dead.
 #pragma unroll
@@ -262,6 +249,28 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
                 const int sl = lane + kWave * i;
                 if ((sl % kZMaxSlots) >= a.zcr)
                     zlive[sl] = 0;
+            }
+            // One wave wrote the list; make its LDS writes visible to its own
+            // later reads from other lanes.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            constexpr int G = 8;                      // gathers in flight per lane
+            const int pairs = nlive * ntok;
+            const uint16_t *xt = a.x + (size_t)tt * ZTOK * a.K;
+            for (int p0 = 0; p0 < pairs; p0 += G * kWave) {
+                uint32_t v[G], dst[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int p = min(p0 + g * kWave + lane, pairs - 1);
+                    const int e = p / ntok, t = p - (p / ntok) * ntok;
+                    const uint32_t le = zlist[e];
+                    dst[g] = (le & 0xffffu) * ZTOK + t;
+                    v[g] = xt[(size_t)t * a.K + (le >> 16)];
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    if (p0 + g * kWave + lane < pairs)
+                        (&zx[0][0])[dst[g]] = bf16_to_f32(v[g]);
             }
           }
         }

@@ -1,4 +1,5 @@
-// FP32-weight (router) skinny variants, one or two 16-token sub-tiles.
+// FP32-weight (router) skinny variants: one or two 16-token sub-tiles, one or
+// two 16-row blocks per workgroup.
 #include "skinny.h"
 #include "variants.h"
 
@@ -9,6 +10,8 @@ namespace gdp {
 const SkinnyVariant kSkinnyPartF32[] = {
     GDP_WAVES_SPW(GDP_ENTRY, 1, 1, 1)
     GDP_WAVES_SPW(GDP_ENTRY, 2, 1, 1)
+    GDP_WAVES_SPW(GDP_ENTRY, 1, 2, 1)
+    GDP_WAVES_SPW(GDP_ENTRY, 2, 2, 1)
 };
 const int kSkinnyPartF32Count = sizeof(kSkinnyPartF32) / sizeof(kSkinnyPartF32[0]);
 

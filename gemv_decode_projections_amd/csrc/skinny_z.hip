@@ -1,4 +1,4 @@
-// Skinny variants reading the 12-bit weights (one 16-token sub-tile).
+// Skinny variants reading the 12-bit weights (one or two 16-token sub-tiles).
 #include "skinny.h"
 #include "variants.h"
 
@@ -14,9 +14,16 @@ namespace gdp {
     GDP_ENTRY(1, RB, 4, 32, 0) GDP_ENTRY(1, RB, 8, 2, 0) GDP_ENTRY(1, RB, 8, 4, 0) GDP_ENTRY(1, RB, 8, 8, 0)  \
     GDP_ENTRY(1, RB, 8, 16, 0) GDP_ENTRY(1, RB, 8, 32, 0)
 
+// Two 16-token sub-tiles (17-32 tokens in one pass over the weights).
+#define GDP_Z_SET2(RB)                                                                                       \
+    GDP_ENTRY(2, RB, 4, 8, 0) GDP_ENTRY(2, RB, 4, 16, 0) GDP_ENTRY(2, RB, 4, 32, 0) GDP_ENTRY(2, RB, 8, 8, 0) \
+    GDP_ENTRY(2, RB, 8, 16, 0) GDP_ENTRY(2, RB, 8, 32, 0)
+
 const SkinnyVariant kSkinnyPartZ[] = {
     GDP_Z_SET(1)
     GDP_Z_SET(2)
+    GDP_Z_SET2(1)
+    GDP_Z_SET2(2)
 };
 const int kSkinnyPartZCount = sizeof(kSkinnyPartZ) / sizeof(kSkinnyPartZ[0]);
 

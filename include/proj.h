@@ -164,7 +164,7 @@ int proj_last_hip_error(void);
  *   flags     bit 0 set: workgroup i keeps tile i. Clear (default): when the
  *             grid is a multiple of 8, consecutive tiles are grouped on one
  *             XCD (workgroups are dealt to the 8 XCDs round-robin).
- *             bit 2 set (kind 0 with nt 1 and waves > 1): read the 12-bit
+ *             bit 2 set (kind 0 with nt 1 or 2 and waves 4 or 8): read the 12-bit
  *             weights (needs proj_compressed(layer) >= 0); the workgroup gets
  *             one more wave, which gathers the correction terms.
  * proj_plan fills the configuration proj_run would use; proj_run_config runs
