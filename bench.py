@@ -42,7 +42,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
 # Pages' H200 per-load time for decode 1, best reported (guide ch. 1 §1.8 table).
 H200_DECODE1_US = 38.25
-PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_decode1.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_loads.json")
 LOAD_ORDER = ("decode-1", "decode-16", "decode-32", "verify-1", "verify-16", "verify-32")
 
 
@@ -50,15 +50,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# Sources that determine the decode-1 (m = 1) kernels and the weight layout
-# they read; the dispatch choice itself is checked by kernel name.
-DECODE1_SOURCES = ("common.h", "repack.h", "skinny.h", "rowdot.h", "skinny_bf16_nt1.hip", "skinny_bf16_nt2.hip",
-                   "skinny_f32.hip", "rowdot_variants.hip")
+# Every kernel source (kernels, weight layouts, the 12-bit encoder, the
+# measurement kernels that scale the counters); the dispatch choice itself is
+# also checked by kernel name.
+def kernel_sources():
+    d = os.path.join(ROOT, "gemv_decode_projections_amd", "csrc")
+    return sorted(n for n in os.listdir(d) if n.endswith((".h", ".hip")))
 
 
 def source_hash():
     h = hashlib.sha256()
-    for name in DECODE1_SOURCES:
+    for name in kernel_sources():
         with open(os.path.join(ROOT, "gemv_decode_projections_amd", "csrc", name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -311,33 +313,72 @@ def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps):
     return out
 
 
-def summarize_pmc(fetch_csv, write_csv, copy_bytes=64 << 20):
-    """HBM bytes per decode-1 launch from the two counter passes of `bench.py --pmc-pass`.
+PMC_REPS = 3
 
-    Each counter is scaled by what it reads on the copy kernel of known size
-    in the same pass (copy_bytes read and copy_bytes written).
-    """
+
+def pmc_sequence():
+    """(load, layer) of the projection launches of `bench.py --pmc-pass`, in order."""
     from workload import LAYERS
 
+    return [(name, l) for _ in range(PMC_REPS) for name in LOAD_ORDER for l in LAYERS]
+
+
+def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20):
+    """HBM bytes (and MFMA use) per launch of every (load, layer) from the counter
+    passes of `bench.py --pmc-pass`.
+
+    FETCH_SIZE and WRITE_SIZE are scaled by what they read on the copy kernel
+    of known size in the same pass (copy_bytes read and copy_bytes written).
+    The optional third pass holds MfmaUtil (MFMA-busy cycles over all SIMD
+    cycles of the dispatch, percent) and SQ_INSTS_VALU_MFMA_MOPS_BF16.
+    """
+    from gemv_decode_projections_amd import roofline as rf
+    from workload import LOADS
+
+    seq = pmc_sequence()
     res = {"source_hash": source_hash(), "copy_bytes": copy_bytes, "launches": {}}
-    for path, cname, key in ((fetch_csv, "FETCH_SIZE", "fetch"), (write_csv, "WRITE_SIZE", "write")):
+
+    def launches(path, cname):
         rows = sorted((r for r in _read_csv(path) if r["Counter_Name"] == cname),
                       key=lambda r: int(r["Dispatch_Id"]))
         sk = [r for r in rows if _is_proj_kernel(r["Kernel_Name"])]
+        if len(sk) != len(seq):
+            raise SystemExit("%s: %d projection launches, the pass makes %d" % (path, len(sk), len(seq)))
+        return rows, sk
+
+    def entry(name, layer, r=None):
+        m = LOADS[name]
+        key = "%s@%d" % (layer, m)
+        if key not in res["launches"]:
+            res["launches"][key] = {"load": name, "kernel": r["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
+                                    "grid": int(r["Grid_Size"]), "algorithmic_bytes": rf.bytes_of(layer, m)}
+        return res["launches"][key]
+
+    for path, cname, key in ((fetch_csv, "FETCH_SIZE", "fetch"), (write_csv, "WRITE_SIZE", "write")):
+        rows, sk = launches(path, cname)
         cp = [float(r["Counter_Value"]) for r in rows if "copy_kernel" in r["Kernel_Name"]]
         scale = copy_bytes / (statistics.median(cp) * 1024.0)
         res[key + "_scale"] = round(scale, 4)
-        for i, layer in enumerate(LAYERS):
-            vals = [float(r["Counter_Value"]) * 1024.0 * scale for r in sk[i::len(LAYERS)]]
-            ent = res["launches"].setdefault("%s@1" % layer, {
-                "kernel": sk[i]["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
-                "grid": int(sk[i]["Grid_Size"])})
-            ent[key + "_bytes"] = round(statistics.median(vals))
+        vals = {}
+        for (name, layer), r in zip(seq, sk):
+            vals.setdefault((name, layer), []).append(float(r["Counter_Value"]) * 1024.0 * scale)
+            entry(name, layer, r)
+        for (name, layer), v in vals.items():
+            entry(name, layer)[key + "_bytes"] = round(statistics.median(v))
+    if mfma_csv:
+        for cname, key in (("MfmaUtil", "mfma_util_pct"), ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "mfma_mops_bf16")):
+            _, sk = launches(mfma_csv, cname)
+            vals = {}
+            for (name, layer), r in zip(seq, sk):
+                vals.setdefault((name, layer), []).append(float(r["Counter_Value"]))
+            for (name, layer), v in vals.items():
+                entry(name, layer)[key] = round(statistics.median(v), 2)
     return res
 
 
 def pmc_pass():
-    """Short deterministic pass for rocprofv3 --pmc: the decode-1 kernels plus a copy of known size."""
+    """Short deterministic pass for rocprofv3 --pmc: every load's kernels, cold,
+    PMC_REPS times, then a copy of known size (the counters' scale)."""
     import torch
 
     from gemv_decode_projections_amd import binding as B
@@ -346,13 +387,14 @@ def pmc_pass():
     n = 64 << 20
     src = torch.ones(n, dtype=torch.uint8, device=b.dev)
     dst = torch.empty(n, dtype=torch.uint8, device=b.dev)
+    for name, layer in pmc_sequence():
+        b.kernel_us(layer, b.LOADS[name])
+    torch.cuda.synchronize()
     for _ in range(3):
-        for layer in b.LAYERS:
-            b.kernel_us(layer, 1)
         B.proj_bench_flush(b.flush, b.sink)
         B.proj_bench_copy(src, dst, n)
-        torch.cuda.synchronize()
-    log("pmc pass done: decode-1 kernels x3, copy of %d bytes x3" % n)
+    torch.cuda.synchronize()
+    log("pmc pass done: every load's kernels x%d, copy of %d bytes x3" % (PMC_REPS, n))
 
 
 def main():
@@ -370,8 +412,9 @@ def main():
                     help="print per-layer durations of the timed steps from a rocprofv3 trace of bench.py")
     ap.add_argument("--summarize-loads-trace", metavar="KERNEL_TRACE_CSV",
                     help="print per-(load, layer) kernel durations from a rocprofv3 trace of bench.py")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="print HBM bytes per launch from the two --pmc passes")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print HBM bytes per launch from the --pmc passes: FETCH_SIZE csv, WRITE_SIZE csv "
+                         "and optionally the MfmaUtil csv")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -382,6 +425,8 @@ def main():
                                                args.graph_reps), indent=1))
         return
     if args.summarize_pmc:
+        if len(args.summarize_pmc) not in (2, 3):
+            raise SystemExit("--summarize-pmc takes FETCH_CSV WRITE_CSV [MFMA_CSV]")
         print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
         return
 
@@ -439,8 +484,12 @@ def main():
         tot = sum(lay.values())
         nbytes = sum(rf.bytes_of(l, m) for l in layers)
         flops = sum(rf.flops_of(l, m) for l in layers)
+        # The hand-written read kernel over each shape's algorithmic bytes.
+        lfloor = {l: floor[l] if m == 1 else b.floor_us(rf.bytes_of(l, m), 9) for l in layers}
         loads[name] = {
             "m": m, "us": round(tot, 2), "layers_us": lay,
+            "read_floor_us": {l: round(v, 2) for l, v in lfloor.items()},
+            "frac_of_read_floor": {l: round(lfloor[l] / lay[l], 3) for l in layers},
             "TBps": round(nbytes / tot / 1e6, 3),
             "TFLOPs": round(flops / tot / 1e6, 2),
             "mfma_frac": round(flops / tot / 1e6 / MFMA_BF16_TFLOPS, 4),
