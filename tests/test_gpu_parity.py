@@ -260,26 +260,45 @@ def test_layers_keep_a_12bit_form():
     assert binding.proj_compressed("router") == -1
 
 
+# (m, 16-token blocks, row blocks, waves, largest k-steps per wave): one and
+# two token blocks, one and two row blocks, with and without a K split across
+# workgroups (the corrections of a slot are applied only by its split).
+_Z_CASES = [(1, 1, 1, 8, 32), (5, 1, 1, 8, 32), (16, 1, 1, 8, 32), (16, 1, 1, 4, 8),
+            (24, 2, 2, 4, 32), (32, 2, 1, 8, 16)]
+
+
+def _z_config(layer, nt, rb, waves, spw_max):
+    ks_total = SHAPES[layer][1] // 32
+    spw_min = 2 if nt == 1 else 8             # smallest compiled 12-bit stage depth
+    if ks_total // waves < spw_min:
+        waves = 4
+    spw = min(spw_max, ks_total // waves)
+    return binding.ProjConfig.make(kind=0, nt=nt, rb=rb, waves=waves, spw=spw,
+                                   ksplit=ks_total // (waves * spw), flags=4)
+
+
 @pytest.mark.parametrize("layer", ["qkv_gate", "o", "pooler", "unpooler"])
-@pytest.mark.parametrize("m", [1, 5, 16])
-def test_12bit_exception_columns_bit_exact(layer, m):
+@pytest.mark.parametrize("case", _Z_CASES, ids=lambda c: "m%d-nt%d-rb%d-w%d" % c[:4])
+def test_12bit_exception_columns_bit_exact(layer, case):
     """A one-hot activation row on a column holding out-of-table weights returns
     that weight column times the scale bit for bit through the 12-bit path
     (report round 5: the corrections restore the original weights exactly);
     the other rows are ordinary inputs checked against the oracle."""
+    m = case[0]
     p = prepared(0)
     w = p.w[layer]
     cols, exc = _exception_columns(w)
     assert cols, "weights without any out-of-table value"
     n_eff = binding.proj_out_cols(layer, m)
-    cfg = binding.ProjConfig.make(kind=0, nt=1, rb=1, waves=8, spw=SHAPES[layer][1] // 256, ksplit=1, flags=4)
+    cfg = _z_config(layer, *case[1:])
     for k in cols:
         xs = make_x(layer, m, seed=1200 + k)
         bits = xs.bits.copy()
         bits[0, :] = 0
         bits[0, k] = bf16_bits_from_f32(np.array([2.0 ** -3], dtype=np.float32))[0]
         xs.bits = bits
-        say("12-bit exception column", layer, "m=%d" % m, "k=%d" % k, "rows with exceptions", int(exc[:n_eff, k].sum()))
+        say("12-bit exception column", layer, "m=%d" % m, "k=%d" % k, "rows with exceptions", int(exc[:n_eff, k].sum()),
+            cfg.as_dict())
         got = run_layer(layer, bits, cfg=cfg)
         want = f32_from_bf16_bits(w[:n_eff, k]).astype(np.float64) * 2.0 ** -3
         assert np.array_equal(got[0], want)
