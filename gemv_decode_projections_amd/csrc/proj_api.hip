@@ -264,7 +264,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         const WideVariant *v = find_wide(c.rb, c.nt, c.spw, f32w);
         if (!v || c.waves != 4)
             return PROJ_ERR_UNSUPPORTED;
-        if (ne % (kRowsPerBlock * c.rb) != 0 || c.ksplit > KS / 2)
+        if (ne % (kRowsPerBlock * c.rb) != 0 || c.ksplit > KS / wide_superstep(c.spw))
             return PROJ_ERR_UNSUPPORTED;
         const int n_rt = ne / (kRowsPerBlock * c.rb);
         const int n_tt = (m + 16 * c.nt - 1) / (16 * c.nt);
@@ -389,28 +389,37 @@ proj_config plan_default(int layer, int m)
     }
     // Larger m: the tiled kernel (kind 1) or the wide-tile kernel (kind 3),
     // picked per layer from measured cold-cache sweeps. Buckets: m <= 64,
-    // m <= 128, larger. Entries: kind, 16-row blocks per tile (rb), 16-token
-    // blocks (nt), weight prefetch depth in k-steps, K split. Past 256 tokens
-    // the split shrinks until the grid is at most ~3 workgroups per compute
-    // unit and the partials fit the workspace.
+    // m <= 128, m <= 256, larger. Entries: kind, 16-row blocks per tile (rb),
+    // 16-token blocks (nt), weight prefetch depth in k-steps, K split. Past
+    // 256 tokens a tile takes 128 tokens once 64-token tiles would give more
+    // than one workgroup per compute unit (the deep-prefetch variants hold 64
+    // tokens, so the depth drops to 8 there), and the split shrinks until the
+    // grid is at most ~3 workgroups per compute unit and the partials fit the
+    // workspace. A split of 0 means: as many splits (at most 4) as keep the
+    // grid within one workgroup per compute unit.
     struct TEntry {
         int kind, rb, nt, depth, ksplit;
     };
-    static const TEntry ttable[PROJ_ROUTER][3] = {   // the four BF16 layers
-        /* qkv_gate */ {{3, 4, 2, 8, 3}, {3, 4, 4, 8, 3}, {3, 8, 4, 8, 3}},
-        /* o        */ {{1, 4, 2, 8, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 4, 1}},
-        /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 8, 2}},
-        /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 8, 1}},
+    static const TEntry ttable[PROJ_ROUTER][4] = {   // the four BF16 layers
+        /* qkv_gate */ {{3, 4, 2, 8, 3}, {3, 4, 4, 8, 3}, {3, 8, 4, 8, 3}, {3, 8, 4, 16, 0}},
+        /* o        */ {{1, 4, 2, 8, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 4, 1}, {3, 8, 4, 4, 0}},
+        /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 16, 2}, {3, 8, 4, 16, 0}},
+        /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 16, 1}, {3, 8, 4, 16, 0}},
     };
-    const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : 2)];
+    const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : (m <= 256 ? 2 : 3))];
     const int ne = n_eff_of(layer, m);
     c.kind = e.kind;
     c.rb = e.rb;
     c.nt = e.nt;
     c.waves = 4;
     c.spw = e.depth;
-    const long tiles = (long)(ne / (16 * c.rb)) * ((m + 16 * c.nt - 1) / (16 * c.nt));
-    int ks = e.ksplit;
+    const long n_rt = ne / (16 * c.rb);
+    if (m > 256 && n_rt * ((m + 63) / 64) > 256) {
+        c.nt = 8;
+        c.spw = e.depth < 8 ? e.depth : 8;
+    }
+    const long tiles = n_rt * ((m + 16 * c.nt - 1) / (16 * c.nt));
+    int ks = e.ksplit > 0 ? e.ksplit : (int)std::max(1L, std::min(4L, 256 / tiles));
     while (ks > 1 && (tiles * ks > 768 || tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes))
         ks = e.kind == 3 ? ks - 1 : ks / 2;   // the tiled kernel splits K into equal powers of two
     c.ksplit = ks;

@@ -76,6 +76,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uin
 // XCDs (each with its own L2) see one another.
 constexpr int kCoherent = 16;
 
+// k-steps per activation super-step for a weight prefetch depth: 2, or 4 at
+// depth 16 (the tail after the last whole pass needs no activation loads
+// only while D / S <= 4).
+constexpr int wide_superstep(int depth) { return depth >= 16 ? 4 : 2; }
+
 template <int RBW, int BNB, int D, int S, bool F32W>
 __global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
 {

@@ -1,13 +1,15 @@
 // Wide-tile kernel variants: (row blocks per wave, token blocks, weight
 // prefetch depth D in k-steps, FP32 weights). A workgroup tile is
-// (64*RBW) x (16*BNB); activations move in super-steps of 2 k-steps.
+// (64*RBW) x (16*BNB); activations move in super-steps of 2 k-steps, or of 4
+// with the depth-16 prefetch (the pipeline keeps at most 4 super-steps of
+// weights ahead).
 #include "variants.h"
 #include "wide.h"
 
 namespace gdp {
 
 #define GDP_WIDE(RBW, BNB, D, F) \
-    {RBW * 4, BNB, D, F, reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, 2, (F != 0)>)},
+    {RBW * 4, BNB, D, F, reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0)>)},
 
 const WideVariant kWideVariants[] = {
     GDP_WIDE(1, 2, 8, 0)
@@ -16,6 +18,8 @@ const WideVariant kWideVariants[] = {
     GDP_WIDE(2, 2, 8, 0)
     GDP_WIDE(2, 4, 4, 0)
     GDP_WIDE(2, 4, 8, 0)
+    GDP_WIDE(2, 4, 16, 0)
+    GDP_WIDE(1, 4, 16, 0)
     GDP_WIDE(2, 8, 4, 0)
     GDP_WIDE(2, 8, 8, 0)
     GDP_WIDE(4, 4, 4, 0)

@@ -93,7 +93,7 @@ def test_dispatch_plans_tile_every_layer(lib):
             else:
                 # wide tiles: 4 waves, whole 64-row blocks, any split up to one super-step each
                 assert cfg.kind == 3 and m > 32 and cfg.waves == 4 and cfg.rb % 4 == 0
-                assert 1 <= cfg.ksplit <= k // 64
+                assert 1 <= cfg.ksplit <= k // (128 if cfg.spw >= 16 else 64)
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
             assert cfg.grid == ne // (16 * cfg.rb) * n_tt * cfg.ksplit
