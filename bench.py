@@ -59,11 +59,18 @@ def kernel_sources():
 
 
 def source_hash():
+    """Hash of the kernel sources with comments and blank space removed (a
+    comment edit does not change a kernel)."""
+    import re
+
     h = hashlib.sha256()
     for name in kernel_sources():
-        with open(os.path.join(ROOT, "gemv_decode_projections_amd", "csrc", name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gemv_decode_projections_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -9,7 +9,7 @@
 // flight while the current one is multiplied; both carry over here.
 //
 // gfx950 design:
-//   * W is pre-packed in fragment-major order (see repack.hip): for each
+//   * W is pre-packed in fragment-major order (see repack.h): for each
 //     16-row block, K/32 fragments of 1 KB (BF16) or 2 KB (FP32), each one
 //     exactly the A operand of v_mfma_f32_16x16x32_bf16 for 64 lanes. A wave
 //     therefore reads 1 KB contiguous per 16-byte-per-lane load.
