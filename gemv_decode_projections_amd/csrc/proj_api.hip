@@ -171,6 +171,11 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
     const LayerState &st = g_layers[layer];
     if (c.ksplit < 1)
         return PROJ_ERR_UNSUPPORTED;
+    // Flag bits each kind understands: 0 placement (all), 2 12-bit weights
+    // (kind 0), 3 stream mode (kind 3).
+    const int known = 1 | (c.kind == 0 ? 4 : 0) | (c.kind == 3 ? 8 : 0);
+    if (c.flags & ~known)
+        return PROJ_ERR_UNSUPPORTED;
     if (c.kind == 0) {
         const int z = (c.flags & 4) ? 1 : 0;
         if (z && st.zcr < 0)
@@ -260,22 +265,44 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
     if (c.kind == 3) {
         // rb = 16-row blocks per tile (4 waves x rb/4), nt = 16-token blocks,
         // spw = weight prefetch depth in k-steps; K split unevenly in
-        // super-steps of 2 k-steps.
+        // super-steps of 2 (4 at depth 16) k-steps. flags bit 3: stream mode,
+        // ksplit = number of workgroups sharing all tiles' super-steps.
         const WideVariant *v = find_wide(c.rb, c.nt, c.spw, f32w);
         if (!v || c.waves != 4)
             return PROJ_ERR_UNSUPPORTED;
-        if (ne % (kRowsPerBlock * c.rb) != 0 || c.ksplit > KS / wide_superstep(c.spw))
+        if (ne % (kRowsPerBlock * c.rb) != 0 || c.ksplit < 1)
             return PROJ_ERR_UNSUPPORTED;
+        const int nss = KS / wide_superstep(c.spw);
         const int n_rt = ne / (kRowsPerBlock * c.rb);
         const int n_tt = (m + 16 * c.nt - 1) / (16 * c.nt);
-        const long long grid = (long long)n_rt * n_tt * c.ksplit;
+        const long long tiles = (long long)n_rt * n_tt;
+        const bool stream = (c.flags & 8) != 0;
+        long long grid = 0;
+        int slots = c.ksplit;                          // workspace slots per tile
+        if (!stream) {
+            if (c.ksplit > nss)
+                return PROJ_ERR_UNSUPPORTED;
+            grid = tiles * c.ksplit;
+        } else {
+            // Every share non-empty (G <= tiles * nss); slots = the most
+            // workgroups any tile is shared by.
+            const long long I = tiles * nss;
+            const long long G = c.ksplit;
+            if (G > I || G > 0x7fffffffLL)
+                return PROJ_ERR_UNSUPPORTED;
+            auto owner = [&](long long q) { return ((q + 1) * G + I - 1) / I - 1; };
+            slots = 1;
+            for (long long t = 0; t < tiles; ++t)
+                slots = std::max(slots, (int)(owner(t * nss + nss - 1) - owner(t * nss) + 1));
+            grid = G;
+        }
         if (grid < 1 || grid > 0x7fffffffLL)
             return PROJ_ERR_UNSUPPORTED;
-        if (c.ksplit > 1) {
+        if (slots > 1) {
             const long long tile_bytes = (long long)c.rb * c.nt * kWave * 16;
-            if ((long long)n_rt * n_tt * c.ksplit * tile_bytes > (long long)kWsBytes)
+            if (tiles * slots * tile_bytes > (long long)kWsBytes)
                 return PROJ_ERR_UNSUPPORTED;
-            if ((long long)n_rt * n_tt > (long long)kCounters)
+            if (tiles > (long long)kCounters)
                 return PROJ_ERR_UNSUPPORTED;
         }
         L.fn = v->fn;
@@ -295,6 +322,8 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         A.n_tt = n_tt;
         A.ksplit = c.ksplit;
         A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
+        A.stream = stream ? 1 : 0;
+        A.maxc = slots;
         return PROJ_OK;
     }
     if (c.kind == 2) {

@@ -61,9 +61,18 @@ struct WideArgs {
     int n_eff;
     int n_rt;                // row tiles
     int n_tt;                // token tiles
-    int ksplit;
+    int ksplit;              // splits per tile; with stream: the number of workgroups
     int xcd_remap;
+    int stream;              // 1: the tiles' super-steps are dealt evenly to the workgroups
+    int maxc;                // stream: most workgroups sharing one tile (workspace slots per tile)
 };
+
+// Stream mode: the first workgroup whose share of I super-steps (G
+// workgroups, workgroup w owns [w*I/G, (w+1)*I/G)) holds super-step p.
+__device__ __forceinline__ int stream_owner(long p, long I, int G)
+{
+    return (int)(((p + 1) * G + I - 1) / I) - 1;
+}
 
 // Raw buffer descriptor over [p, p + bytes) (gfx9 dword 3: 32-bit data).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes)
@@ -112,20 +121,15 @@ __global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
     const int lane = tid % kWave;
     const int wave = tid / kWave;
 
-    // Workgroup -> (split, token tile, row tile), split fastest.
+    // Logical workgroup id; consecutive ids (one tile's splits, or the
+    // neighbouring shares of stream mode) sit on one XCD.
     const int G = gridDim.x;
     int L = blockIdx.x;
     if (a.xcd_remap)
         L = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
-    const int ks = L % a.ksplit;
-    const int rest = L / a.ksplit;
-    const int tt = rest % a.n_tt;
-    const int rt = rest / a.n_tt;
 
     const int KS = a.K / kStepK;
     const int NSS = KS / S;                           // super-steps in the whole row
-    const int tok0 = tt * BNB * 16;
-    const int rbw0 = rt * BMB + wave * RBW;           // first row block of this wave
 
     const u32x4 *wbase = reinterpret_cast<const u32x4 *>(a.wp);
 
@@ -134,17 +138,25 @@ __global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
     // bytes. Chunk c is k-step c/4, k-group c%4 of the super-step.
     const uint16_t *xsrc[XPT];
     int xdst[XPT];
+    int tok0 = 0, rbw0 = 0, rt = 0;
+    // Per-tile state: tile = row tile * n_tt + token tile.
+    auto set_tile = [&](int tile) {
+        const int tt = tile % a.n_tt;
+        rt = tile / a.n_tt;
+        tok0 = tt * BNB * 16;
+        rbw0 = rt * BMB + wave * RBW;                 // first row block of this wave
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const int u = i * NTHR + tid;
-        const int c = u % CPT;
-        const int qt = u / CPT;                       // token within the tile
-        const int blk = qt / 16, q = qt % 16;
-        const int sub = c / 4, g = c % 4;
-        const int tok = tok0 + qt;
-        xsrc[i] = (tok < a.m ? a.x + (size_t)tok * a.K : a.zrow) + 8 * c;
-        xdst[i] = sub * REG + blk * kWave + 4 * q + ((g + q / 4) & 3);
-    }
+        for (int i = 0; i < XPT; ++i) {
+            const int u = i * NTHR + tid;
+            const int c = u % CPT;
+            const int qt = u / CPT;                   // token within the tile
+            const int blk = qt / 16, q = qt % 16;
+            const int sub = c / 4, g = c % 4;
+            const int tok = tok0 + qt;
+            xsrc[i] = (tok < a.m ? a.x + (size_t)tok * a.K : a.zrow) + 8 * c;
+            xdst[i] = sub * REG + blk * kWave + 4 * q + ((g + q / 4) & 3);
+        }
+    };
     // LDS unit holding (token l%16, k-group l/16) of a fragment for this lane.
     const int bslot = 4 * (lane % 16) + (((lane / 16) + (lane % 16) / 4) & 3);
 
@@ -277,108 +289,141 @@ __global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
                 body(jj, j0 + jj, false);
     };
 
-    // This split's super-steps.
-    const int ss_begin = (int)(((long)ks * NSS) / a.ksplit);
-    const int ss_count = (int)(((long)(ks + 1) * NSS) / a.ksplit) - ss_begin;
-    run(ss_begin, ss_count);
-
-    const int tile = rt * a.n_tt + tt;
-    if (a.ksplit > 1) {
-        // Publish this split's partial tile (write-through 16-byte stores,
-        // each wave's stores 1 KB contiguous), wait until they are complete,
-        // count the arrival; the last workgroup of the tile sums the splits.
-        // acc (r, t) covers rows (rbw0 + r)*16 + 4*(lane/16) + 0..3 and
-        // token tok0 + t*16 + lane%16.
-        constexpr int TILE_U = BMB * BNB * kWave;     // 16-byte words per partial tile
-        const uint32_t tile_off = (uint32_t)tile * a.ksplit * TILE_U * 16u;
-        auto unit_of = [&](int r, int t) { return ((wave * RBW + r) * BNB + t) * kWave + lane; };
-        const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(a.ws, a.ws_bytes);
+    // Sum the parts of one tile and store it. slot: this workgroup's part
+    // (parts are summed in slot order), nparts: workgroups holding a part.
+    auto finish = [&](int tile, int slot, int nparts) {
+        const int slots = a.stream ? a.maxc : a.ksplit;
+        if (nparts > 1) {
+            // Publish this part (write-through 16-byte stores, each wave's
+            // stores 1 KB contiguous), wait until they are complete, count the
+            // arrival; the last workgroup of the tile sums all parts. acc
+            // (r, t) covers rows (rbw0 + r)*16 + 4*(lane/16) + 0..3 and token
+            // tok0 + t*16 + lane%16.
+            constexpr int TILE_U = BMB * BNB * kWave;     // 16-byte words per partial tile
+            const uint32_t tile_off = (uint32_t)tile * slots * TILE_U * 16u;
+            auto unit_of = [&](int r, int t) { return ((wave * RBW + r) * BNB + t) * kWave + lane; };
+            const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(a.ws, a.ws_bytes);
 #pragma unroll
-        for (int r = 0; r < RBW; ++r)
+            for (int r = 0; r < RBW; ++r)
 #pragma unroll
-            for (int t = 0; t < BNB; ++t)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[r][t]), ws,
-                                                       tile_off + ((uint32_t)ks * TILE_U + unit_of(r, t)) * 16u,
-                                                       0, kCoherent);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) {
-            const uint32_t prev =
-                __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (prev == (uint32_t)(a.ksplit - 1));
-            if (s_last)
-                __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        if (!s_last)
-            return;
-        // Sum in split order; this workgroup's own split comes from registers
-        // (the same bits it published). CH splits are gathered per round
-        // with every load in flight.
-        constexpr int CH = (RBW * BNB >= 16) ? 2 : (RBW * BNB >= 8 ? 4 : 8);
-        f32x4 sum[RBW][BNB];
+                for (int t = 0; t < BNB; ++t)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[r][t]), ws,
+                                                           tile_off + ((uint32_t)slot * TILE_U + unit_of(r, t)) * 16u,
+                                                           0, kCoherent);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) {
+                const uint32_t prev =
+                    __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_last = (prev == (uint32_t)(nparts - 1));
+                if (s_last)
+                    __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (!s_last)
+                return;
+            // Sum in slot order; this workgroup's own part comes from
+            // registers (the same bits it published). CH parts are gathered
+            // per round with every load in flight.
+            constexpr int CH = (RBW * BNB >= 16) ? 2 : (RBW * BNB >= 8 ? 4 : 8);
+            f32x4 sum[RBW][BNB];
 #pragma unroll
-        for (int r = 0; r < RBW; ++r)
+            for (int r = 0; r < RBW; ++r)
 #pragma unroll
-            for (int t = 0; t < BNB; ++t)
-                sum[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < a.ksplit; c0 += CH) {
-            u32x4 part[CH][RBW][BNB];
+                for (int t = 0; t < BNB; ++t)
+                    sum[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c0 = 0; c0 < nparts; c0 += CH) {
+                u32x4 part[CH][RBW][BNB];
 #pragma unroll
-            for (int ci = 0; ci < CH; ++ci) {
-                const int sp = min(c0 + ci, a.ksplit - 1);   // past the end: re-read, never summed
+                for (int ci = 0; ci < CH; ++ci) {
+                    const int sp = min(c0 + ci, nparts - 1);   // past the end: re-read, never summed
 #pragma unroll
-                for (int r = 0; r < RBW; ++r)
+                    for (int r = 0; r < RBW; ++r)
 #pragma unroll
-                    for (int t = 0; t < BNB; ++t)
-                        part[ci][r][t] = __builtin_amdgcn_raw_buffer_load_b128(
-                            ws, tile_off + ((uint32_t)sp * TILE_U + unit_of(r, t)) * 16u, 0, kCoherent);
+                        for (int t = 0; t < BNB; ++t)
+                            part[ci][r][t] = __builtin_amdgcn_raw_buffer_load_b128(
+                                ws, tile_off + ((uint32_t)sp * TILE_U + unit_of(r, t)) * 16u, 0, kCoherent);
+                }
+#pragma unroll
+                for (int ci = 0; ci < CH; ++ci) {
+                    const int sp = c0 + ci;
+                    if (sp >= nparts)
+                        break;
+#pragma unroll
+                    for (int r = 0; r < RBW; ++r)
+#pragma unroll
+                        for (int t = 0; t < BNB; ++t)
+                            sum[r][t] += (sp == slot) ? acc[r][t] : __builtin_bit_cast(f32x4, part[ci][r][t]);
+                }
             }
 #pragma unroll
-            for (int ci = 0; ci < CH; ++ci) {
-                const int sp = c0 + ci;
-                if (sp >= a.ksplit)
-                    break;
+            for (int r = 0; r < RBW; ++r)
 #pragma unroll
-                for (int r = 0; r < RBW; ++r)
-#pragma unroll
-                    for (int t = 0; t < BNB; ++t)
-                        sum[r][t] += (sp == ks) ? acc[r][t] : __builtin_bit_cast(f32x4, part[ci][r][t]);
-            }
+                for (int t = 0; t < BNB; ++t)
+                    acc[r][t] = sum[r][t];
         }
+
+        // Stage the output tile token-major in LDS and write whole 16-byte
+        // chunks along each token's output row. The barrier retires the last
+        // reads of the activation ring.
+        __syncthreads();
 #pragma unroll
         for (int r = 0; r < RBW; ++r)
 #pragma unroll
-            for (int t = 0; t < BNB; ++t)
-                acc[r][t] = sum[r][t];
-    }
-
-    // Stage the output tile token-major in LDS and write whole 16-byte
-    // chunks along each token's output row. The barrier retires the last
-    // reads of the activation ring.
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RBW; ++r)
-#pragma unroll
-        for (int t = 0; t < BNB; ++t) {
-            const int tl = t * 16 + (lane % 16);
-            const int rl = (wave * RBW + r) * kRowsPerBlock + 4 * (lane / 16);
-            char *d = lds + tl * ROWP + rl * OB;
-            if constexpr (F32W)
-                *reinterpret_cast<f32x4 *>(d) = acc[r][t];
-            else
-                *reinterpret_cast<u32x2 *>(d) = u32x2{pack_bf16x2(acc[r][t].x, acc[r][t].y),
-                                                      pack_bf16x2(acc[r][t].z, acc[r][t].w)};
+            for (int t = 0; t < BNB; ++t) {
+                const int tl = t * 16 + (lane % 16);
+                const int rl = (wave * RBW + r) * kRowsPerBlock + 4 * (lane / 16);
+                char *d = lds + tl * ROWP + rl * OB;
+                if constexpr (F32W)
+                    *reinterpret_cast<f32x4 *>(d) = acc[r][t];
+                else
+                    *reinterpret_cast<u32x2 *>(d) = u32x2{pack_bf16x2(acc[r][t].x, acc[r][t].y),
+                                                          pack_bf16x2(acc[r][t].z, acc[r][t].w)};
+            }
+        __syncthreads();
+        constexpr int CPR = ROWB / 16;                    // 16-byte chunks per token row
+        char *obase = reinterpret_cast<char *>(a.out) + (size_t)rt * BMB * kRowsPerBlock * OB;
+        for (int c = tid; c < BNB * 16 * CPR; c += NTHR) {
+            const int tl = c / CPR, ck = c % CPR;
+            const int tk = tok0 + tl;
+            if (tk < a.m)
+                *reinterpret_cast<u32x4 *>(obase + (size_t)tk * a.n_eff * OB + ck * 16) =
+                    *reinterpret_cast<const u32x4 *>(lds + tl * ROWP + ck * 16);
         }
-    __syncthreads();
-    constexpr int CPR = ROWB / 16;                    // 16-byte chunks per token row
-    char *obase = reinterpret_cast<char *>(a.out) + (size_t)rt * BMB * kRowsPerBlock * OB;
-    for (int c = tid; c < BNB * 16 * CPR; c += NTHR) {
-        const int tl = c / CPR, ck = c % CPR;
-        const int tk = tok0 + tl;
-        if (tk < a.m)
-            *reinterpret_cast<u32x4 *>(obase + (size_t)tk * a.n_eff * OB + ck * 16) =
-                *reinterpret_cast<const u32x4 *>(lds + tl * ROWP + ck * 16);
+        // The next segment of stream mode refills the ring: every thread
+        // must be past its reads of the staged tile.
+        __syncthreads();
+    };
+
+    if (!a.stream) {
+        // Workgroup -> (split, tile), split fastest; K split unevenly over
+        // a.ksplit workgroups.
+        const int ks = L % a.ksplit;
+        const int tile = L / a.ksplit;
+        set_tile(tile);
+        const int ss_begin = (int)(((long)ks * NSS) / a.ksplit);
+        const int ss_count = (int)(((long)(ks + 1) * NSS) / a.ksplit) - ss_begin;
+        run(ss_begin, ss_count);
+        finish(tile, ks, a.ksplit);
+    } else {
+        // Stream mode: the I = tiles * NSS super-steps are dealt in G equal
+        // contiguous shares (G <= I, so none is empty); a share may end one
+        // tile and begin the next. A tile's parts are summed by whichever of
+        // its workgroups arrives last, in workgroup order.
+        const long I = (long)a.n_rt * a.n_tt * NSS;
+        long it = (long)L * I / G;
+        const long it_end = (long)(L + 1) * I / G;
+        while (it < it_end) {
+            const int tile = (int)(it / NSS);
+            const int s0 = (int)(it - (long)tile * NSS);
+            const int n = (int)min((long)(NSS - s0), it_end - it);
+            const int w0 = stream_owner((long)tile * NSS, I, G);
+            const int w1 = stream_owner((long)tile * NSS + NSS - 1, I, G);
+            set_tile(tile);
+            run(s0, n);
+            finish(tile, L - w0, w1 - w0 + 1);
+            it += n;
+        }
     }
 }
 

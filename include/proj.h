@@ -167,6 +167,13 @@ int proj_last_hip_error(void);
  *             bit 2 set (kind 0 with nt 1 or 2 and waves 4 or 8): read the 12-bit
  *             weights (needs proj_compressed(layer) >= 0); the workgroup gets
  *             one more wave, which gathers the correction terms.
+ *             bit 3 set (kind 3): stream mode. ksplit is then the number of
+ *             workgroups (at most tiles x K/(32 S) super-steps, S = 2, or 4
+ *             at depth 16); the super-steps of all tiles are dealt to them in
+ *             equal contiguous shares, a share may finish one tile and start
+ *             the next, and the workgroups sharing a tile sum their parts in
+ *             workgroup order (the last to arrive stores the tile).
+ *             Other bits, or a bit the kind does not use, are rejected.
  * proj_plan fills the configuration proj_run would use; proj_run_config runs
  * an explicit one and returns PROJ_ERR_UNSUPPORTED if it is not compiled or
  * does not tile the layer.

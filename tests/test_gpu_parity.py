@@ -171,6 +171,48 @@ def test_every_compiled_variant(case):
         assert r.ok, (case, m, r)
 
 
+# Stream mode of the wide-tile kernel: (layer, m, rb, nt, depth, workgroups,
+# flags). Covers the production shape, an uneven share count without XCD
+# grouping, the depth-16 prefetch, one super-step per workgroup (the most
+# parts per tile), one workgroup for the whole layer, 128-token tiles and
+# FP32 weights.
+_STREAM_CASES = [("qkv_gate", 256, 8, 4, 8, 256, 8), ("qkv_gate", 130, 4, 4, 8, 250, 9),
+                 ("pooler", 200, 8, 4, 16, 256, 8), ("o", 33, 8, 4, 4, 1024, 8), ("o", 33, 8, 4, 8, 1, 8),
+                 ("unpooler", 400, 8, 8, 8, 264, 8), ("router", 256, 4, 2, 8, 256, 8)]
+
+
+@pytest.mark.parametrize("case", _STREAM_CASES, ids=lambda c: "%s-m%d-rb%d-nt%d-d%d-g%d-f%d" % c)
+def test_wide_stream_mode(case):
+    """The tiles' K super-steps dealt evenly to the workgroups (a share may end
+    one tile and start the next) give oracle-exact results, and the same
+    input twice gives the same bits (parts summed in workgroup order)."""
+    layer, m, rb, nt, depth, groups, flags = case
+    p = prepared(0)
+    cfg = binding.ProjConfig.make(kind=3, nt=nt, rb=rb, waves=4, spw=depth, ksplit=groups, flags=flags)
+    xs = make_x(layer, m, seed=1400 + m, outliers=True)
+    say("stream", case)
+    got = run_layer(layer, xs.bits, cfg=cfg)
+    r = compare(layer, got, p.w[layer], xs)
+    assert r.ok, (case, r)
+    again = run_layer(layer, xs.bits, cfg=cfg)
+    assert np.array_equal(got, again)
+
+
+def test_wide_stream_mode_rejects_more_workgroups_than_super_steps():
+    prepared(0)
+    m, n_rt, nss = 33, 8192 // 128, 1024 // 32 // 2        # layer o, 128-row tiles, one token tile
+    x = to_device_x(make_x("o", m, seed=3).bits)
+    out = binding.new_out("o", m)
+    ok = binding.ProjConfig.make(kind=3, nt=4, rb=8, waves=4, spw=8, ksplit=n_rt * nss, flags=8)
+    binding.proj_run_config("o", x, m, out, ok)
+    torch.cuda.synchronize()
+    for bad in (binding.ProjConfig.make(kind=3, nt=4, rb=8, waves=4, spw=8, ksplit=n_rt * nss + 1, flags=8),
+                binding.ProjConfig.make(kind=3, nt=4, rb=8, waves=4, spw=8, ksplit=2, flags=16),
+                binding.ProjConfig.make(kind=1, nt=2, rb=4, waves=4, spw=8, ksplit=1, flags=8)):
+        with pytest.raises(binding.ProjError):
+            binding.proj_run_config("o", x, m, out, bad)
+
+
 @pytest.mark.parametrize("layer,m", [("router", 1), ("router", 32), ("unpooler", 8)])
 def test_split_k_across_xcds(layer, m):
     """Split-K groups spread over different XCDs (no workgroup grouping) still reduce correctly."""
