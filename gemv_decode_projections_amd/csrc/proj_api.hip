@@ -305,7 +305,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
             if (tiles > (long long)kCounters)
                 return PROJ_ERR_UNSUPPORTED;
         }
-        L.fn = v->fn;
+        L.fn = stream ? v->fn_stream : v->fn;
         L.kind = 3;
         L.grid = (int)grid;
         L.block = 4 * kWave;
@@ -322,7 +322,6 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         A.n_tt = n_tt;
         A.ksplit = c.ksplit;
         A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
-        A.stream = stream ? 1 : 0;
         A.maxc = slots;
         return PROJ_OK;
     }

@@ -43,7 +43,8 @@ struct WideVariant {
     int bnb;
     int depth;        // weight prefetch distance in k-steps
     int f32w;
-    const void *fn;   // __global__ void (WideArgs)
+    const void *fn;          // __global__ void (WideArgs): one tile per workgroup
+    const void *fn_stream;   // the same kernel in stream mode
 };
 
 // Each part is defined in its own translation unit so the variants compile in parallel.

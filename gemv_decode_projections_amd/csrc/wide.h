@@ -63,7 +63,6 @@ struct WideArgs {
     int n_tt;                // token tiles
     int ksplit;              // splits per tile; with stream: the number of workgroups
     int xcd_remap;
-    int stream;              // 1: the tiles' super-steps are dealt evenly to the workgroups
     int maxc;                // stream: most workgroups sharing one tile (workspace slots per tile)
 };
 
@@ -90,7 +89,9 @@ constexpr int kCoherent = 16;
 // only while D / S <= 4).
 constexpr int wide_superstep(int depth) { return depth >= 16 ? 4 : 2; }
 
-template <int RBW, int BNB, int D, int S, bool F32W>
+// STREAM: stream mode (a separate instantiation, so that the one-tile path
+// keeps its register allocation and schedule).
+template <int RBW, int BNB, int D, int S, bool F32W, bool STREAM>
 __global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
 {
     constexpr int WAVES = 4;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
     // Sum the parts of one tile and store it. slot: this workgroup's part
     // (parts are summed in slot order), nparts: workgroups holding a part.
     auto finish = [&](int tile, int slot, int nparts) {
-        const int slots = a.stream ? a.maxc : a.ksplit;
+        const int slots = STREAM ? a.maxc : a.ksplit;
         if (nparts > 1) {
             // Publish this part (write-through 16-byte stores, each wave's
             // stores 1 KB contiguous), wait until they are complete, count the
@@ -392,10 +393,11 @@ __global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
         }
         // The next segment of stream mode refills the ring: every thread
         // must be past its reads of the staged tile.
-        __syncthreads();
+        if constexpr (STREAM)
+            __syncthreads();
     };
 
-    if (!a.stream) {
+    if constexpr (!STREAM) {
         // Workgroup -> (split, tile), split fastest; K split unevenly over
         // a.ksplit workgroups.
         const int ks = L % a.ksplit;

@@ -8,8 +8,9 @@
 
 namespace gdp {
 
-#define GDP_WIDE(RBW, BNB, D, F) \
-    {RBW * 4, BNB, D, F, reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0)>)},
+#define GDP_WIDE(RBW, BNB, D, F)                                                                       \
+    {RBW * 4, BNB, D, F, reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0), false>), \
+     reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0), true>)},
 
 const WideVariant kWideVariants[] = {
     GDP_WIDE(1, 2, 8, 0)

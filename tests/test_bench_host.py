@@ -18,7 +18,9 @@ def test_kernel_names_match_the_templates():
     assert bench.kernel_name(_cfg(0, 1, 1, 8, 32), False) == "skinny_kernel<1, 1, 8, 32, false, false>"
     assert bench.kernel_name(_cfg(0, 1, 1, 8, 32, flags=4), False) == "skinny_kernel<1, 1, 8, 32, false, true>"
     assert bench.kernel_name(_cfg(0, 2, 1, 4, 16, 4), True) == "skinny_kernel<2, 1, 4, 16, true, false>"
-    assert bench.kernel_name(_cfg(3, 4, 8, 4, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false>"
+    assert bench.kernel_name(_cfg(3, 4, 8, 4, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false>"
+    assert bench.kernel_name(_cfg(3, 4, 8, 4, 16, 2), False) == "wide_kernel<2, 4, 16, 4, false, false>"
+    assert bench.kernel_name(_cfg(3, 2, 4, 4, 8, 256, 8), True) == "wide_kernel<1, 2, 8, 2, true, true>"
     assert bench.kernel_name(_cfg(1, 2, 8, 4, 8), False) == "tiled_kernel<2, 2, 4, 4, 8, false>"
     assert bench.kernel_name(_cfg(2, 8, 1, 4, 4), True) == "rowdot_kernel<8, 1, 4, true>"
 
@@ -90,7 +92,7 @@ def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
                         "End_Timestamp": t + 100000, "Grid_Size_X": 1})
             t += 100000
             dur = 1000 * (LAYERS.index(layer) + 1) + LOADS[name]        # ns
-            w.writerow({"Kernel_Name": "void gdp::wide_kernel<2, 4, 8, 2, false>(a)", "Start_Timestamp": t,
+            w.writerow({"Kernel_Name": "void gdp::wide_kernel<2, 4, 8, 2, false, false>(a)", "Start_Timestamp": t,
                         "End_Timestamp": t + dur, "Grid_Size_X": 256})
             t += dur
     r = bench.summarize_loads_trace(str(path), steps, warmup, load_reps, graph_reps)
@@ -98,6 +100,6 @@ def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
         lay = r[name]["layers"]
         for layer in LAYERS:
             assert lay[layer]["median_us"] == pytest.approx((1000 * (LAYERS.index(layer) + 1) + m) / 1e3)
-            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false>"
+            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false>"
     with pytest.raises(SystemExit):
         bench.summarize_loads_trace(str(path), steps + 1, warmup, load_reps, graph_reps)
