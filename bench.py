@@ -270,14 +270,18 @@ def summarize_trace(trace_csv, steps, warmup):
     return out
 
 
-def call_sequence(steps, warmup, load_reps, graph_reps, graph=True):
-    """(load, layer) of every projection kernel bench.py launches, in launch order."""
-    from workload import LAYERS
+def call_sequence(steps, warmup, load_reps, graph_reps, awkward_reps, graph=True):
+    """(load, layer) of every projection kernel bench.py launches, in launch order
+    (the awkward token counts appear as loads named "m=<m>")."""
+    from workload import AWKWARD_M, LAYERS
 
     seq = [("decode-1", l) for _ in range(warmup + steps) for l in LAYERS]
     for name in LOAD_ORDER[1:]:
         for l in LAYERS:
             seq += [(name, l)] * load_reps
+    for m in AWKWARD_M:
+        for l in LAYERS:
+            seq += [("m=%d" % m, l)] * awkward_reps
     if graph:
         for name in LOAD_ORDER:
             for l in LAYERS:
@@ -285,7 +289,7 @@ def call_sequence(steps, warmup, load_reps, graph_reps, graph=True):
     return seq
 
 
-def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps):
+def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps, awkward_reps):
     """Kernel durations of every (load, layer) from a rocprofv3 kernel trace of bench.py.
 
     The projection launches in the trace (in start order) are matched one to
@@ -297,7 +301,7 @@ def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps):
 
     rows = sorted((r for r in _read_csv(trace_csv) if _is_proj_kernel(r["Kernel_Name"])),
                   key=lambda r: int(r["Start_Timestamp"]))
-    seq = call_sequence(steps, warmup, load_reps, graph_reps)
+    seq = call_sequence(steps, warmup, load_reps, graph_reps, awkward_reps)
     if len(rows) != len(seq):
         raise SystemExit("trace has %d projection launches, the bench sequence %d: counts differ"
                          % (len(rows), len(seq)))
@@ -306,9 +310,11 @@ def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps):
         e = per.setdefault((name, layer), {"kernel": r["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
                                            "grid": int(r["Grid_Size_X"]), "d": []})
         e["d"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    from workload import AWKWARD_M
+
     out = {}
-    for name in LOAD_ORDER:
-        m = LOADS[name]
+    for name in list(LOAD_ORDER) + ["m=%d" % m for m in AWKWARD_M]:
+        m = LOADS[name] if name in LOADS else int(name[2:])
         lay = {}
         for (n2, layer), e in per.items():
             if n2 != name:
@@ -415,6 +421,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
     ap.add_argument("--graph-reps", type=int, default=15)
+    ap.add_argument("--awkward-reps", type=int, default=7, help="cold calls per layer at each awkward token count")
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print per-layer durations of the timed steps from a rocprofv3 trace of bench.py")
@@ -430,7 +437,7 @@ def main():
         return
     if args.summarize_loads_trace:
         print(json.dumps(summarize_loads_trace(args.summarize_loads_trace, args.steps, args.warmup, args.load_reps,
-                                               args.graph_reps), indent=1))
+                                               args.graph_reps, args.awkward_reps), indent=1))
         return
     if args.summarize_pmc:
         if len(args.summarize_pmc) not in (2, 3):
@@ -505,6 +512,15 @@ def main():
         }
         log("%-10s m=%-4d %8.2f us  %s" % (name, m, tot, lay))
 
+    # The awkward token counts of the correctness sweep, timed the same way
+    # (cold, kernel-duration events): per layer and summed over the five.
+    from workload import AWKWARD_M
+    awkward = {}
+    for m in AWKWARD_M:
+        lay = {l: round(statistics.median(b.kernel_us(l, m) for _ in range(args.awkward_reps)), 2) for l in layers}
+        awkward[str(m)] = {"us": round(sum(lay.values()), 2), "layers_us": lay}
+    log("awkward m: %s" % {m: v["us"] for m, v in awkward.items()})
+
     # The pages' own timing method for context: each call captured in a HIP
     # graph and replayed cold, minus the same for a graph of one empty kernel.
     graph = None
@@ -569,6 +585,7 @@ def main():
         "decode1_frac_of_read_floor": round(floor_sum / value, 4),
         "decode1_TBps": round(sum(rf.bytes_of(l, 1) for l in layers) / value / 1e6, 3),
         "loads": loads,
+        "awkward_m": awkward,
         "graph_replay": graph,
         "timed_wall_s": round(wall, 4),
         "roofline": roof,

@@ -415,6 +415,19 @@ proj_config plan_default(int layer, int m)
         c.ksplit = e.ksplit;
         return c;
     }
+    // qkv_gate just past 32 tokens: the 12-bit skinny kernel over 16-token
+    // tiles (each tile re-reads the 12-bit stream, mostly from L2) beat the
+    // tiled kernels up to 48 tokens (m = 33 / 48: 12.4 / 12.7 us against
+    // 13.4 / 13.5) and lost at 64 (17.2 against 13.3).
+    if (layer == PROJ_QKV_GATE && m <= 48 && g_layers[layer].zcr >= 0) {
+        c.nt = 1;
+        c.rb = 2;
+        c.waves = 8;
+        c.spw = 32;
+        c.ksplit = 1;
+        c.flags = 4;
+        return c;
+    }
     // Larger m: the tiled kernel (kind 1) or the wide-tile kernel (kind 3),
     // picked per layer from measured cold-cache sweeps. Buckets: m <= 64,
     // m <= 128, m <= 256, larger. Entries: kind, 16-row blocks per tile (rb),
@@ -424,15 +437,17 @@ proj_config plan_default(int layer, int m)
     // tokens, so the depth drops to 8 there), and the split shrinks until the
     // grid is at most ~3 workgroups per compute unit and the partials fit the
     // workspace. A split of 0 means: as many splits (at most 4) as keep the
-    // grid within one workgroup per compute unit.
+    // grid within one workgroup per compute unit (a grid past 256 measured
+    // far slower: qkv_gate m = 130 with 64-token tiles took 18.7 us at 4
+    // splits, 216 workgroups, 32.4 at 5, 270 workgroups, and 24.5 at 3).
     struct TEntry {
         int kind, rb, nt, depth, ksplit;
     };
     static const TEntry ttable[PROJ_ROUTER][4] = {   // the four BF16 layers
-        /* qkv_gate */ {{3, 4, 2, 8, 3}, {3, 4, 4, 8, 3}, {3, 8, 4, 8, 3}, {3, 8, 4, 16, 0}},
-        /* o        */ {{1, 4, 2, 8, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 4, 1}, {3, 8, 4, 4, 0}},
-        /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 16, 2}, {3, 8, 4, 16, 0}},
-        /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 16, 1}, {3, 8, 4, 16, 0}},
+        /* qkv_gate */ {{3, 4, 2, 8, 3}, {3, 4, 4, 8, 3}, {3, 8, 4, 8, 0}, {3, 8, 4, 16, 0}},
+        /* o        */ {{1, 4, 2, 8, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 4, 0}, {3, 8, 4, 4, 0}},
+        /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 16, 0}, {3, 8, 4, 16, 0}},
+        /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 16, 0}, {3, 8, 4, 16, 0}},
     };
     const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : (m <= 256 ? 2 : 3))];
     const int ne = n_eff_of(layer, m);

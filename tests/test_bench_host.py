@@ -7,7 +7,7 @@ import pytest
 
 import bench
 from gemv_decode_projections_amd import binding, roofline as rf
-from workload import LAYERS, LOADS
+from workload import AWKWARD_M, LAYERS, LOADS
 
 
 def _cfg(kind, nt, rb, waves, spw, ksplit=1, flags=0):
@@ -80,8 +80,8 @@ def test_pmc_summary_refuses_a_pass_with_missing_launches(tmp_path):
 
 
 def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
-    steps, warmup, load_reps, graph_reps = 3, 1, 2, 2
-    seq = bench.call_sequence(steps, warmup, load_reps, graph_reps)
+    steps, warmup, load_reps, graph_reps, awkward_reps = 3, 1, 2, 2, 1
+    seq = bench.call_sequence(steps, warmup, load_reps, graph_reps, awkward_reps)
     path = tmp_path / "trace.csv"
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"])
@@ -91,15 +91,20 @@ def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
             w.writerow({"Kernel_Name": "gdp::(anonymous namespace)::flush_kernel(x)", "Start_Timestamp": t,
                         "End_Timestamp": t + 100000, "Grid_Size_X": 1})
             t += 100000
-            dur = 1000 * (LAYERS.index(layer) + 1) + LOADS[name]        # ns
+            dur = 1000 * (LAYERS.index(layer) + 1) + LOADS.get(name, 999)   # ns
             w.writerow({"Kernel_Name": "void gdp::wide_kernel<2, 4, 8, 2, false, false>(a)", "Start_Timestamp": t,
                         "End_Timestamp": t + dur, "Grid_Size_X": 256})
             t += dur
-    r = bench.summarize_loads_trace(str(path), steps, warmup, load_reps, graph_reps)
+    r = bench.summarize_loads_trace(str(path), steps, warmup, load_reps, graph_reps, awkward_reps)
     for name, m in LOADS.items():
         lay = r[name]["layers"]
         for layer in LAYERS:
             assert lay[layer]["median_us"] == pytest.approx((1000 * (LAYERS.index(layer) + 1) + m) / 1e3)
             assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false>"
+    for m in AWKWARD_M:
+        assert r["m=%d" % m]["m"] == m
+        for layer in LAYERS:
+            assert r["m=%d" % m]["layers"][layer]["median_us"] == pytest.approx((1000 * (LAYERS.index(layer) + 1) + 999) / 1e3)
+            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false>"
     with pytest.raises(SystemExit):
-        bench.summarize_loads_trace(str(path), steps + 1, warmup, load_reps, graph_reps)
+        bench.summarize_loads_trace(str(path), steps + 1, warmup, load_reps, graph_reps, awkward_reps)
