@@ -119,3 +119,17 @@ def test_run_config_rejects_untiled_configs(lib):
     rc = lib.proj_run_config(0, ctypes.c_void_p(16), 1, ctypes.c_void_p(16), ctypes.c_void_p(0),
                              ctypes.byref(cfg))
     assert rc == -5
+
+
+def test_large_m_split_counts_keep_one_workgroup_per_cu(lib):
+    # Past 128 tokens the K split is the largest that keeps the wide kernel's
+    # grid within 256 workgroups (one per compute unit); grids above that only
+    # come from the tiles themselves, without a split.
+    for name in ("qkv_gate", "o", "pooler", "unpooler"):
+        for m in list(range(129, 520, 7)) + [1000, 4096]:
+            cfg = binding.proj_plan(name, m)
+            assert cfg.kind == 3, (name, m)
+            if cfg.ksplit > 1:
+                assert cfg.grid <= 256, (name, m, cfg.as_dict())
+                tiles = cfg.grid // cfg.ksplit
+                assert tiles * (cfg.ksplit + 1) > 256 or cfg.ksplit == 4, (name, m, cfg.as_dict())
