@@ -311,10 +311,9 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     f32x4 *wsp = a.ws + ((size_t)tile * a.ksplit) * ELEMS;
 
     // 12-bit corrections, applied once per (row, token) by its own thread
-    // (spread over the whole workgroup, so each thread's chain of dependent
-    // LDS reads is one row long): zfin = sum of the waves' partials in wave
-    // order, then for each live slot of the row in slot order
-    // v = (v - d*x) + w*x.
+    // (the pairs are spread over the whole workgroup): zfin = sum of the
+    // waves' partials in wave order, then for each live slot of the row in
+    // slot order v = (v - d*x) + w*x.
     constexpr int ZROWS = 16 * RB;
     __shared__ float zfin[Z ? ZROWS : 1][Z ? ZTOK : 1];
     if constexpr (Z && WAVES > 1) {
