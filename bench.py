@@ -327,6 +327,101 @@ def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps, awkwa
     return out
 
 
+PROFILE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench "
+               "-o bench -- python3 -u $REPO/bench.py --no-cpu-baseline")
+PMC_CMDS = (
+    "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o fetch "
+    "-- python3 $REPO/bench.py --pmc-pass",
+    "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o write "
+    "-- python3 $REPO/bench.py --pmc-pass",
+    "cd /tmp && rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d $REPO/gpurun_out/pmc_mfma "
+    "-o mfma -- python3 $REPO/bench.py --pmc-pass",
+)
+
+
+def md_decode1_trace(tr, trace_csv, bench_line=None, steps=50, warmup=5):
+    """profiles/decode1_kernels_trace.md from summarize_trace()'s result (and,
+    when given, the JSON line of the same bench run without the profiler)."""
+    from gemv_decode_projections_amd import roofline as rf
+
+    L = ["# Decode-1 kernels: rocprofv3 kernel trace of bench.py (MI355X, 1 GPU)", "",
+         "Commands (repo root on the GPU box; `$REPO` is its path):", "", "```", PROFILE_CMD,
+         "python bench.py --summarize-trace %s --md --bench-json gpurun_out/bench.json > profiles/decode1_kernels_trace.md"
+         % trace_csv,
+         "python bench.py --summarize-loads-trace %s --md > profiles/loads_kernels_trace.md" % trace_csv, "```", "",
+         "Timed region: the %d decode-1 steps after %d warmup steps (each call preceded by a 1 GiB flush)." % (steps, warmup),
+         "Kernel durations are the trace's start/end stamps."]
+    if bench_line:
+        ev, roof = bench_line["decode1_layers_us"], bench_line["roofline"]
+        dom = roof["layer"]
+        L += ["The same bench command run without the profiler (and with the CPU baseline), in the same session,",
+              "reported (hipExtLaunchKernel events, median): " + ", ".join("%s %.2f" % (l, v) for l, v in ev.items())
+              + " us; dominant kernel %s (`%s`) event average %.3f us vs trace mean %.3f us." % (
+                  dom, roof["kernel"], roof["avg_us"], tr[dom]["mean_us"]),
+              "(Under the profiler the events themselves read longer per call, because tracing adds work around each",
+              "dispatch; the trace stamps do not include it.)"]
+        if roof.get("weights") == "12-bit lossless":
+            L += ["", "Kernels whose last template argument is `true` read 12-bit lossless weights; the dominant one (%s)"
+                  % dom, "reads %d bytes (%.3f of the BF16 bytes). Algorithmic bytes and GB/s below count the BF16 operation."
+                  % (roof["stored_bytes"], roof["stored_bytes"] / roof["algorithmic_bytes"])]
+    L += ["", "| layer | kernel | grid (threads) | n | mean us | median us | algorithmic bytes | GB/s (mean) |",
+          "|---|---|---|---|---|---|---|---|"]
+    for l, e in tr.items():
+        by = rf.bytes_of(l, 1)
+        L.append("| %s | `%s` | %d | %d | %.3f | %.3f | %d | %d |" % (l, e["kernel"], e["grid"], e["n"], e["mean_us"],
+                                                                     e["median_us"], by, round(by / e["mean_us"] / 1e3)))
+    L += ["", "Sum of the five trace medians: %.2f us per decode-1 load." % sum(e["median_us"] for e in tr.values()), ""]
+    return "\n".join(L)
+
+
+def md_loads_trace(lt, trace_csv):
+    """profiles/loads_kernels_trace.md from summarize_loads_trace()'s result."""
+    L = ["# Every load's kernels: rocprofv3 kernel trace of bench.py (MI355X, 1 GPU)", "",
+         "Same trace as `decode1_kernels_trace.md` (command there); table from",
+         "`python bench.py --summarize-loads-trace %s --md`." % trace_csv,
+         "Every launch is cold (1 GiB flush before it). Launches are matched in order with the bench's launch",
+         "sequence (`bench.call_sequence`); n counts the event-timed calls, the graph warm-up run and the replays;",
+         "loads named m=<m> are the awkward token counts. TB/s and TFLOP/s use algorithmic bytes and FLOPs",
+         "(guide ch. 1 §1.7 formulas).", "",
+         "| load | m | layer | kernel | grid (threads) | n | median us | TB/s | TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for ld, d in lt.items():
+        for l, e in d["layers"].items():
+            L.append("| %s | %d | %s | `%s` | %d | %d | %.3f | %.3f | %.1f |" % (
+                ld, d["m"], l, e["kernel"], e["grid"], e["n"], e["median_us"], e["TBps"], e["TFLOPs"]))
+    L += ["", "Per-load sums of the trace medians (us): "
+          + ", ".join("%s %.2f" % (ld, d["sum_median_us"]) for ld, d in lt.items()) + ".", ""]
+    return "\n".join(L)
+
+
+def md_pmc(pm, csvs):
+    """profiles/pmc_loads.md from summarize_pmc()'s result."""
+    L = ["# HBM traffic and MFMA use per launch, every load: rocprofv3 --pmc (MI355X, 1 GPU)", "",
+         "Commands (repo root on the GPU box; one counter set per run):", "", "```"] + list(PMC_CMDS) + [
+         "python bench.py --summarize-pmc %s > profiles/pmc_loads.json" % " ".join(csvs),
+         "python bench.py --summarize-pmc %s --md > profiles/pmc_loads.md" % " ".join(csvs), "```", "",
+         "The pass runs every load's five kernels cold (1 GiB flush before each), %d times, then copies 64 MiB three"
+         % PMC_REPS,
+         "times. FETCH_SIZE reads %.4f x fewer KiB than that copy moves and WRITE_SIZE reads it with scale %.4f; both"
+         % (pm["fetch_scale"], pm["write_scale"]),
+         "are multiplied by their scale. Medians of the %d passes. MFMA util = MFMA-busy cycles over all SIMD cycles"
+         % PMC_REPS,
+         "of the dispatch (rocprofv3's MfmaUtil); MOPS = SQ_INSTS_VALU_MFMA_MOPS_BF16 as counted. Kernels whose last",
+         "template argument is `true` read 12-bit lossless weights (3/4 of the BF16 bytes plus a correction table).",
+         "FETCH_SIZE counts what the L2 caches fetch from memory (HBM or the Infinity Cache behind them); each XCD's",
+         "L2 fetches its own copy of data that workgroups on several XCDs read (x at large m).", "",
+         "| load | layer | kernel | fetched by L2 (FETCH_SIZE, bytes) | written (WRITE_SIZE, bytes) | algorithmic bytes "
+         "| traffic / algorithmic | MFMA util % | MFMA MOPS (bf16) |",
+         "|---|---|---|---|---|---|---|---|---|"]
+    for key, e in pm["launches"].items():
+        L.append("| %s | %s | `%s` | %d | %d | %d | %.3f | %s | %s |" % (
+            e["load"], key.split("@")[0], e["kernel"], e["fetch_bytes"], e["write_bytes"], e["algorithmic_bytes"],
+            (e["fetch_bytes"] + e["write_bytes"]) / e["algorithmic_bytes"], e.get("mfma_util_pct", "-"),
+            e.get("mfma_mops_bf16", "-")))
+    L += ["", "Source hash of the kernels these counters belong to: `%s` (bench.py reports `traffic` = null once the "
+          "sources differ)." % pm["source_hash"], ""]
+    return "\n".join(L)
+
+
 PMC_REPS = 3
 
 
@@ -427,22 +522,34 @@ def main():
                     help="print per-layer durations of the timed steps from a rocprofv3 trace of bench.py")
     ap.add_argument("--summarize-loads-trace", metavar="KERNEL_TRACE_CSV",
                     help="print per-(load, layer) kernel durations from a rocprofv3 trace of bench.py")
+    ap.add_argument("--md", action="store_true", help="with --summarize-*: print the profiles/ Markdown page")
+    ap.add_argument("--bench-json", metavar="PATH", help="with --summarize-trace --md: the bench line of the same run")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="print HBM bytes per launch from the --pmc passes: FETCH_SIZE csv, WRITE_SIZE csv "
                          "and optionally the MfmaUtil csv")
     args = ap.parse_args()
 
     if args.summarize_trace:
-        print(json.dumps(summarize_trace(args.summarize_trace, args.steps, args.warmup), indent=1))
+        tr = summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        if args.md:
+            line = None
+            if args.bench_json:
+                with open(args.bench_json) as f:
+                    line = json.loads(f.read().strip().splitlines()[-1])
+            print(md_decode1_trace(tr, args.summarize_trace, line, args.steps, args.warmup))
+        else:
+            print(json.dumps(tr, indent=1))
         return
     if args.summarize_loads_trace:
-        print(json.dumps(summarize_loads_trace(args.summarize_loads_trace, args.steps, args.warmup, args.load_reps,
-                                               args.graph_reps, args.awkward_reps), indent=1))
+        lt = summarize_loads_trace(args.summarize_loads_trace, args.steps, args.warmup, args.load_reps,
+                                   args.graph_reps, args.awkward_reps)
+        print(md_loads_trace(lt, args.summarize_loads_trace) if args.md else json.dumps(lt, indent=1))
         return
     if args.summarize_pmc:
         if len(args.summarize_pmc) not in (2, 3):
             raise SystemExit("--summarize-pmc takes FETCH_CSV WRITE_CSV [MFMA_CSV]")
-        print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
+        pm = summarize_pmc(*args.summarize_pmc)
+        print(md_pmc(pm, args.summarize_pmc) if args.md else json.dumps(pm, indent=1))
         return
 
     if args.gpus != 1:

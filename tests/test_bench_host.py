@@ -108,3 +108,16 @@ def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
             assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false>"
     with pytest.raises(SystemExit):
         bench.summarize_loads_trace(str(path), steps + 1, warmup, load_reps, graph_reps, awkward_reps)
+
+
+def test_profile_pages_render(tmp_path):
+    copy_kib = (64 << 20) / 1024 / 2
+    _pmc_csv(tmp_path / "f.csv", ["FETCH_SIZE"], lambda n, l, c: rf.bytes_of(l, LOADS[n]) / 2048.0, copy_kib)
+    _pmc_csv(tmp_path / "w.csv", ["WRITE_SIZE"], lambda n, l, c: 8.0, 64 << 10)
+    pm = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    page = bench.md_pmc(pm, ["f.csv", "w.csv"])
+    assert page.count("\n| ") >= len(LOADS) * len(LAYERS) and "rocprofv3 --pmc FETCH_SIZE" in page
+    tr = {l: {"kernel": "skinny_kernel<1, 1, 8, 32, false, false>", "grid": 64, "n": 3, "mean_us": 5.0,
+              "median_us": 5.0} for l in LAYERS}
+    page = bench.md_decode1_trace(tr, "t.csv")
+    assert "Sum of the five trace medians: 25.00 us" in page and "--kernel-trace" in page
