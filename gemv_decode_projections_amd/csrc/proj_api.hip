@@ -43,13 +43,14 @@ constexpr int kSliceRows = 1024;
 // the chip with the MFMA kernels).
 constexpr int kRowMajorRows[PROJ_NUM_LAYERS] = {0, 0, 0, kSliceRows, 256};
 
-constexpr size_t kWsBytes = 32u << 20;       // split-K partials per layer
+constexpr size_t kWsBytes = 32u << 20;       // split-K partials per layer (each of the two workspaces)
 constexpr size_t kCounters = 1u << 16;       // split-K arrival counters per layer
 
 struct LayerState {
     void *wp = nullptr;
-    f32x4 *ws = nullptr;
+    f32x4 *ws = nullptr;          // tiled / wide split-K partials (arrival counters)
     uint32_t *counters = nullptr;
+    uint64_t *pws = nullptr;      // skinny split-K partials (polled; all ones between launches)
     uint16_t *zrow = nullptr;     // K zero BF16 values: activation rows past m
     void *wrow = nullptr;         // row-major copy of the first wrow_rows rows (row-dot kernel)
     int wrow_rows = 0;
@@ -196,8 +197,6 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
             const long long elems = (long long)c.rb * c.nt * kWave;
             if ((long long)n_rt * n_tt * c.ksplit * elems * (long long)sizeof(f32x4) > (long long)kWsBytes)
                 return PROJ_ERR_UNSUPPORTED;
-            if ((long long)n_rt * n_tt > (long long)kCounters)
-                return PROJ_ERR_UNSUPPORTED;
         }
         L.fn = v->fn;
         L.kind = 0;
@@ -211,8 +210,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         A.zcr = z ? st.zcr : 0;
         A.zexc = st.zexc;
         A.wp = st.wp;
-        A.ws = st.ws;
-        A.counters = st.counters;
+        A.pws = st.pws;
         A.m = m;
         A.K = li.K;
         A.n_eff = ne;
@@ -587,6 +585,8 @@ void free_layer(LayerState &st)
         (void)hipFree(st.ws);
     if (st.counters)
         (void)hipFree(st.counters);
+    if (st.pws)
+        (void)hipFree(st.pws);
     if (st.zrow)
         (void)hipFree(st.zrow);
     if (st.wrow)
@@ -627,6 +627,8 @@ int proj_prepare(int layer, const void *W)
         (e = hipMalloc(reinterpret_cast<void **>(&ns.ws), kWsBytes)) != hipSuccess ||
         (e = hipMalloc(reinterpret_cast<void **>(&ns.counters), kCounters * sizeof(uint32_t))) != hipSuccess ||
         (e = hipMemset(ns.counters, 0, kCounters * sizeof(uint32_t))) != hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void **>(&ns.pws), kWsBytes)) != hipSuccess ||
+        (e = hipMemset(ns.pws, 0xff, kWsBytes)) != hipSuccess ||
         (e = hipMalloc(reinterpret_cast<void **>(&ns.zrow), (size_t)li.K * 2)) != hipSuccess ||
         (e = hipMemset(ns.zrow, 0, (size_t)li.K * 2)) != hipSuccess) {
         free_layer(ns);

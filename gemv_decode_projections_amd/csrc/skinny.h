@@ -22,10 +22,12 @@
 //     wave starts its run at a rotated k-step (spreads activation requests
 //     over L2 channels).
 //   * The waves' partial 16x16 tiles are summed through LDS in wave order.
-//   * With KSPLIT > 1 workgroups of one tile write FP32 partials to a
-//     workspace with cache-coherent atomic stores; the last to arrive sums
-//     them in split order (deterministic), stores the output and resets the
-//     tile's counter for the next launch.
+//   * With KSPLIT > 1 one workgroup of each tile, the one the hardware
+//     dispatches last, reduces; the others write their FP32 partials to a
+//     workspace with cache-coherent atomic stores and exit. The reducer polls
+//     those words until none holds the empty mark (all bits set), sums the
+//     partials in split order with its own in place (deterministic), stores
+//     the output and puts the mark back for the next launch.
 //   * FP32 router weights are split exactly into three BF16 parts in
 //     registers (common.h) and accumulated by three MFMAs in FP32.
 //   * Z: weights read in the 12-bit lossless form (common.h, decode12; the
@@ -50,8 +52,7 @@ struct SkinnyArgs {
     const void *wp;          // packed weights
     const uint16_t *x;       // m x K BF16
     void *out;               // m x n_eff (BF16 or FP32)
-    f32x4 *ws;               // split-K partials
-    uint32_t *counters;      // split-K arrival counters, zero between launches
+    uint64_t *pws;           // split-K partials; every word all ones between launches
     int m;
     int K;
     int n_eff;
@@ -95,6 +96,29 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     const int rest = L / a.n_tt;
     const int ks = rest % a.ksplit;
     const int rt = rest / a.ksplit;
+
+    // Split-K reducing split (used after the main loop; computed here, off
+    // the critical path): the one with the highest hardware id. Without the XCD
+    // remap that is the last; with it, logical id l runs on hardware id
+    // 8 * (l % (G/8)) + l / (G/8), walked here over the tile's splits (logical
+    // stride n_tt) with one division.
+    int rs = a.ksplit - 1;
+    if (a.xcd_remap) {
+        const int per = G / 8;
+        const int l0 = rt * a.ksplit * a.n_tt + tt;
+        int q = l0 / per, r = l0 - q * per, best = -1;
+        for (int s = 0; s < a.ksplit; ++s) {
+            if (8 * r + q > best) {
+                best = 8 * r + q;
+                rs = s;
+            }
+            r += a.n_tt;
+            while (r >= per) {
+                r -= per;
+                ++q;
+            }
+        }
+    }
 
     const int KS = a.K / kStepK;                     // k-steps in the whole row
     const int step0 = (ks * WAVES + wave) * SPW;     // this wave's first k-step
@@ -295,7 +319,6 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     constexpr int TILES = RB * NT;
     constexpr int ELEMS = TILES * kWave;             // f32x4 per workgroup tile
     __shared__ f32x4 red[WAVES > 1 ? WAVES : 1][TILES][kWave];
-    __shared__ int s_last;
     if constexpr (WAVES > 1) {
         if (!exc_wave) {
 #pragma unroll
@@ -308,7 +331,6 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     }
 
     const int tile = rt * a.n_tt + tt;
-    f32x4 *wsp = a.ws + ((size_t)tile * a.ksplit) * ELEMS;
 
     // 12-bit corrections, applied once per (row, token) by its own thread
     // (the pairs are spread over the whole workgroup): zfin = sum of the
@@ -409,55 +431,97 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
         return;
     }
 
-    // Cross-workgroup split: publish this split's partial tile, count arrivals,
-    // and let the last workgroup of the tile sum all partials in split order.
-    // Partials and the counter use agent-scope atomics, which the compiler
-    // maps to cache-coherent (write-through / L2-bypassing) accesses on this
-    // multi-XCD part; no L2 write-back or invalidate is needed. Each wave
-    // waits until its partial stores are complete before the barrier, so the
-    // arrival that thread 0 counts afterwards covers the whole workgroup.
-    // Values move as 8-byte words (an f32x4 is two words, low element first).
-    // The last workgroup gathers WAVES splits per round, one per wave, with
-    // all of a wave's loads in flight at once, and sums them through LDS.
+    // Cross-workgroup split. The reducer is the split whose hardware id is
+    // highest: dispatch is in id order, so every workgroup it waits for has
+    // been placed on the chip before it and runs to completion without
+    // waiting on anything. The other splits publish their partial tile (8-byte
+    // words, an f32x4 is two words, low element first) with agent-scope
+    // atomic stores, which the compiler maps to cache-coherent write-through
+    // accesses on this multi-XCD part, and exit. No store acknowledgement,
+    // arrival counter or L2 write-back/invalidate is needed: a word that is
+    // not all ones has arrived. A partial whose bits are all ones (one NaN
+    // pattern) is published as the default NaN so that it cannot read as
+    // empty. The reducer gathers WAVES splits per round, one per wave: once
+    // one word of the split has arrived it loads them all at once, re-reads
+    // the words still empty, marks every word empty again, and sums through
+    // LDS in split order, taking its own partial from registers at its place.
+    // The poll is bounded: after kPollLimit rounds the missing words count as
+    // NaN, so a launch always ends (and a lost partial shows in the output).
     constexpr int EPT = (ELEMS + NTHR - 1) / NTHR;  // output elements per thread
-    uint64_t *wsw = reinterpret_cast<uint64_t *>(wsp);
-    for (int e = threadIdx.x; e < ELEMS; e += NTHR) {
-        // Whole-vector bit cast: a bit cast of one vector element reads element 0.
-        const u32x4 u = __builtin_bit_cast(u32x4, wave_sum(e));
-        uint64_t *d = wsw + ((size_t)ks * ELEMS + e) * 2;
-        __hip_atomic_store(d, (uint64_t)u.x | ((uint64_t)u.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(d + 1, (uint64_t)u.z | ((uint64_t)u.w << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t prev = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (uint32_t)(a.ksplit - 1));
-    }
-    __syncthreads();
-    if (!s_last)
+    constexpr uint64_t kEmpty = ~0ull;
+    constexpr int kPollLimit = 1 << 18;
+    uint64_t *wsw = a.pws + (size_t)tile * a.ksplit * ELEMS * 2;
+    if (ks != rs) {
+        for (int e = threadIdx.x; e < ELEMS; e += NTHR) {
+            u32x4 u = __builtin_bit_cast(u32x4, wave_sum(e));
+            u.x = u.x == 0xffffffffu ? 0x7fc00000u : u.x;
+            u.y = u.y == 0xffffffffu ? 0x7fc00000u : u.y;
+            u.z = u.z == 0xffffffffu ? 0x7fc00000u : u.z;
+            u.w = u.w == 0xffffffffu ? 0x7fc00000u : u.w;
+            uint64_t *d = wsw + ((size_t)ks * ELEMS + e) * 2;
+            __hip_atomic_store(d, (uint64_t)u.x | ((uint64_t)u.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(d + 1, (uint64_t)u.z | ((uint64_t)u.w << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
         return;
+    }
+    f32x4 own[EPT];
     f32x4 v[EPT];
 #pragma unroll
-    for (int i = 0; i < EPT; ++i)
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * NTHR;
+        own[i] = e < ELEMS ? wave_sum(e) : f32x4{0.f, 0.f, 0.f, 0.f};
         v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int s0 = 0; s0 < a.ksplit; s0 += WAVES) {
-        // Waves past the last split re-read it (valid memory, never summed).
-        const int sp = min(s0 + wave, a.ksplit - 1);
-        const uint64_t *src = wsw + (size_t)sp * ELEMS * 2;
-        uint64_t wd[TILES][2];
-#pragma unroll
-        for (int j = 0; j < TILES; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                wd[j][h] = __hip_atomic_load(src + (j * kWave + lane) * 2 + h, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+        const int sp = s0 + wave;
         __syncthreads();                             // earlier readers of red are done
-        if (!exc_wave) {
+        if (!exc_wave && sp < a.ksplit && sp != rs) {
+            uint64_t *src = wsw + (size_t)sp * ELEMS * 2;
+            // Wait on one word first (one request per wave and round), so
+            // that waiting reducers add little traffic to the streams of the
+            // splits still running; then read all and re-read stragglers.
+            int poll = 0;
+            while (__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kEmpty && poll < kPollLimit)
+                ++poll;
+            uint64_t wd[TILES][2];
+#pragma unroll
+            for (int j = 0; j < TILES; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wd[j][h] = __hip_atomic_load(src + (j * kWave + lane) * 2 + h, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            for (;; ++poll) {
+                bool miss = false;
+#pragma unroll
+                for (int j = 0; j < TILES; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        miss |= wd[j][h] == kEmpty;
+                if (!__any(miss))
+                    break;
+                if (poll >= kPollLimit) {
+#pragma unroll
+                    for (int j = 0; j < TILES; ++j)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            wd[j][h] = wd[j][h] == kEmpty ? 0x7fc000007fc00000ull : wd[j][h];
+                    break;
+                }
+#pragma unroll
+                for (int j = 0; j < TILES; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        if (wd[j][h] == kEmpty)
+                            wd[j][h] = __hip_atomic_load(src + (j * kWave + lane) * 2 + h, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            }
 #pragma unroll
             for (int j = 0; j < TILES; ++j) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    __hip_atomic_store(src + (j * kWave + lane) * 2 + h, kEmpty, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
                 const u32x4 u = {(uint32_t)wd[j][0], (uint32_t)(wd[j][0] >> 32), (uint32_t)wd[j][1],
                                  (uint32_t)(wd[j][1] >> 32)};
                 red[wave][j][lane] = __builtin_bit_cast(f32x4, u);
@@ -470,7 +534,7 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
             const int e = threadIdx.x + i * NTHR;
             if (e < ELEMS)
                 for (int w = 0; w < nw; ++w)
-                    v[i] += red[w][e / kWave][e % kWave];
+                    v[i] += (s0 + w == rs) ? own[i] : red[w][e / kWave][e % kWave];
         }
     }
 #pragma unroll
@@ -479,8 +543,6 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
         if (e < ELEMS)
             store_out(e, v[i]);
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace gdp

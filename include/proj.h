@@ -72,7 +72,7 @@ enum proj_status {
  *    for layers 0..3 and FP32 for the router. Read only during the call; the
  *    caller keeps ownership and may free it on return.
  * Effect: allocates library-owned device memory for the packed copy (same
- *    byte count as W) and the layer's split-K workspace, runs the repack on
+ *    byte count as W) and the layer's split-K workspaces (2 x 32 MB), runs the repack on
  *    the null stream and synchronizes the device. For the router (all 256
  *    rows) and the unpooler (its first 1024 rows) it also keeps a plain
  *    row-major copy of those rows for the row-dot kernel used at m <= 8
@@ -94,8 +94,9 @@ int proj_prepare(int layer, const void *W);
  * Effect: exactly one kernel launch on `stream`. No allocation, no
  *    synchronization, no host read of device memory, no memset; the choice
  *    of kernel depends on (layer, m) only. Safe to capture in a HIP graph and
- *    replay with new contents of x. Split-K counters (if the chosen kernel
- *    uses them) are reset on the GPU by the kernel itself.
+ *    replay with new contents of x. Split-K state (arrival counters, or the
+ *    empty marks of the polled partials) is restored on the GPU by the
+ *    kernel itself.
  * Errors (checked on the host before launching): PROJ_ERR_LAYER, PROJ_ERR_M,
  *    PROJ_ERR_NULL, PROJ_ERR_ALIGN, PROJ_ERR_NOT_PREPARED, PROJ_ERR_DEVICE;
  *    PROJ_ERR_HIP if the launch is rejected.

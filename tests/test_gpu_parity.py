@@ -229,6 +229,65 @@ def test_split_k_across_xcds(layer, m):
         assert r.ok, (rep, r)
 
 
+def _split_configs(layer):
+    """Skinny splits of 2..16 workgroups (XCD-grouped and not) and a tiled split, all at 32 tokens."""
+    ks_all = SHAPES[layer][1] // 32
+    mk = binding.ProjConfig.make
+    cfgs = [mk(kind=0, nt=2, rb=1, waves=8, spw=ks_all // (8 * ks), ksplit=ks, flags=f)
+            for ks in (2, 4, 8, 16) for f in (0, 1)]
+    cfgs.append(mk(kind=1, nt=2, rb=4, waves=4, spw=8, ksplit=4, flags=0))
+    return cfgs
+
+
+@pytest.mark.parametrize("layer", ["router", "qkv_gate"])
+def test_split_workspaces_clean_between_kernels(layer):
+    """Skinny splits poll their partials for an empty mark that the reducer puts
+    back; tiled splits count arrivals. Interleaving both, with different split
+    counts over the same tiles, never shows a stale partial: every rerun is bit
+    identical to the first run of its configuration, which matches the oracle."""
+    p = prepared(0)
+    m = 32
+    xs = make_x(layer, m, seed=950, outliers=True)
+    first = {}
+    cfgs = _split_configs(layer)
+    for rnd in range(3):
+        for i, cfg in enumerate(cfgs if rnd % 2 == 0 else cfgs[::-1]):
+            key = str(cfg.as_dict())
+            got = run_layer(layer, xs.bits, cfg=cfg)
+            if key not in first:
+                r = compare(layer, got, p.w[layer], xs)
+                assert r.ok, (key, r)
+                first[key] = got
+            else:
+                assert np.array_equal(got, first[key], equal_nan=True), (rnd, key)
+
+
+def test_split_partial_with_all_ones_bits_is_not_lost():
+    """A weight whose bits are all ones (a NaN) makes the partials of its row
+    NaN; the polled reduction still ends at once, that row reads NaN and every
+    other row is bit identical to a run without it."""
+    import time
+    _dirty()
+    w = make_weight("router", 0).copy()
+    w[5, 1000] = 0.0
+    m = 16
+    xs = make_x("router", m, seed=960)
+    cfgs = [binding.proj_plan("router", m)] + [c for c in _split_configs("router") if c.kind == 0][:4]
+    binding.proj_prepare("router", to_device_weight("router", w))
+    clean = [run_layer("router", xs.bits, cfg=c) for c in cfgs]
+    w[5, 1000] = np.uint32(0xFFFFFFFF).view(np.float32)
+    binding.proj_prepare("router", to_device_weight("router", w))
+    for c, ref in zip(cfgs, clean):
+        t0 = time.perf_counter()
+        got = run_layer("router", xs.bits, cfg=c)
+        dt = time.perf_counter() - t0
+        assert dt < 0.05, (c.as_dict(), dt)
+        assert np.isnan(got[:, 5]).all(), c.as_dict()
+        keep = np.arange(got.shape[1]) != 5
+        assert np.array_equal(got[:, keep], ref[:, keep]), c.as_dict()
+    _dirty()
+
+
 @pytest.mark.parametrize("layer", LAYERS)
 def test_output_rows_beyond_m_untouched(layer):
     prepared(0)
