@@ -371,7 +371,7 @@ proj_config plan_default(int layer, int m)
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
         {{1, 1, 8, 16, 1, 0}, {1, 2, 8, 16, 1, 1}, {2, 2, 4, 32, 1, 0}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
-        {{1, 1, 8, 4, 8, 0}, {1, 1, 16, 2, 8, 0}, {1, 1, 8, 4, 8, 0}},
+        {{1, 1, 8, 4, 8, 0}, {1, 1, 8, 4, 8, 0}, {1, 1, 8, 4, 8, 0}},
     };
     proj_config c{};
     // Few tokens on the router (m <= 8) and the unpooler slice (m <= 4):
@@ -401,10 +401,10 @@ proj_config plan_default(int layer, int m)
     // The router past 32 tokens stays on the skinny kernel: with 16 row
     // blocks the tiled kernels' 64-row tiles leave most compute units idle
     // or need deep K splits (measured 12-15 us against 8-13.5 here). Two
-    // 16-token blocks per workgroup from 65 tokens, two row blocks past 256.
+    // 16-token blocks per workgroup from 65 tokens, two row blocks from 129.
     if (layer == PROJ_ROUTER) {
         static const Entry rtable[4] = {
-            {1, 1, 16, 4, 4, 0}, {2, 1, 16, 4, 4, 0}, {2, 1, 4, 16, 4, 0}, {2, 2, 4, 16, 4, 0}};
+            {1, 1, 16, 4, 4, 0}, {2, 1, 16, 4, 4, 0}, {2, 2, 16, 4, 4, 0}, {2, 2, 4, 16, 4, 0}};
         const Entry &e = rtable[m <= 64 ? 0 : m <= 128 ? 1 : m <= 256 ? 2 : 3];
         c.nt = e.nt;
         c.rb = e.rb;
