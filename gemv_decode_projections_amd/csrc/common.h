@@ -95,4 +95,48 @@ __device__ __forceinline__ void split3_f32(const u32x4 &w0, const u32x4 &w1, u32
     }
 }
 
+// Polled split-K over workgroups (the skinny kernel): the workspace
+// holds every split's FP32 partial tile, and a 32-bit word with all bits set
+// means "not written yet" (the library fills the workspace with that mark
+// once; each reduction puts it back). One split per tile, the one the
+// hardware dispatches last, reduces: it polls the others' words with loads
+// that bypass the XCD-local L2 until none holds the mark. The other splits
+// only publish and exit, so no arrival counter, store acknowledgement or
+// cache flush is needed.
+constexpr uint32_t kEmptyWord = 0xffffffffu;
+constexpr int kPollLimit = 1 << 18;   // polls before a reducer gives up (missing words read as NaN)
+
+// The one NaN pattern that equals the mark is published as the default NaN.
+__device__ __forceinline__ uint32_t publishable(uint32_t u) { return u == kEmptyWord ? 0x7fc00000u : u; }
+__device__ __forceinline__ u32x4 publishable(u32x4 u)
+{
+    return u32x4{publishable(u.x), publishable(u.y), publishable(u.z), publishable(u.w)};
+}
+
+// Index, among the n logical workgroup ids l0, l0 + stride, ..., of the one
+// with the highest hardware id: the reducer of a tile. Dispatch runs in
+// hardware-id order, so every workgroup the reducer waits for has been
+// placed on the chip before it and finishes without waiting itself. With the
+// XCD remap (G % 8 == 0) logical id l runs on hardware id
+// 8 * (l % (G / 8)) + l / (G / 8); the walk uses one division.
+__device__ __forceinline__ int reducing_split(int l0, int stride, int n, int G, bool remap)
+{
+    if (!remap)
+        return n - 1;
+    const int per = G / 8;
+    int q = l0 / per, r = l0 - q * per, best = -1, rs = n - 1;
+    for (int s = 0; s < n; ++s) {
+        if (8 * r + q > best) {
+            best = 8 * r + q;
+            rs = s;
+        }
+        r += stride;
+        while (r >= per) {
+            r -= per;
+            ++q;
+        }
+    }
+    return rs;
+}
+
 }  // namespace gdp

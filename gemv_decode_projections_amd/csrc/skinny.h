@@ -97,28 +97,10 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     const int ks = rest % a.ksplit;
     const int rt = rest / a.ksplit;
 
-    // Split-K reducing split (used after the main loop; computed here, off
-    // the critical path): the one with the highest hardware id. Without the XCD
-    // remap that is the last; with it, logical id l runs on hardware id
-    // 8 * (l % (G/8)) + l / (G/8), walked here over the tile's splits (logical
-    // stride n_tt) with one division.
-    int rs = a.ksplit - 1;
-    if (a.xcd_remap) {
-        const int per = G / 8;
-        const int l0 = rt * a.ksplit * a.n_tt + tt;
-        int q = l0 / per, r = l0 - q * per, best = -1;
-        for (int s = 0; s < a.ksplit; ++s) {
-            if (8 * r + q > best) {
-                best = 8 * r + q;
-                rs = s;
-            }
-            r += a.n_tt;
-            while (r >= per) {
-                r -= per;
-                ++q;
-            }
-        }
-    }
+    // Split-K reducer of this tile (used after the main loop, computed here
+    // off the critical path).
+    const int rs = a.ksplit > 1 ? reducing_split(rt * a.ksplit * a.n_tt + tt, a.n_tt, a.ksplit, G, a.xcd_remap)
+                                : 0;
 
     const int KS = a.K / kStepK;                     // k-steps in the whole row
     const int step0 = (ks * WAVES + wave) * SPW;     // this wave's first k-step
@@ -431,33 +413,23 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
         return;
     }
 
-    // Cross-workgroup split. The reducer is the split whose hardware id is
-    // highest: dispatch is in id order, so every workgroup it waits for has
-    // been placed on the chip before it and runs to completion without
-    // waiting on anything. The other splits publish their partial tile (8-byte
+    // Cross-workgroup split (common.h: polled partials, reducer = the split
+    // dispatched last). The other splits publish their partial tile (8-byte
     // words, an f32x4 is two words, low element first) with agent-scope
     // atomic stores, which the compiler maps to cache-coherent write-through
-    // accesses on this multi-XCD part, and exit. No store acknowledgement,
-    // arrival counter or L2 write-back/invalidate is needed: a word that is
-    // not all ones has arrived. A partial whose bits are all ones (one NaN
-    // pattern) is published as the default NaN so that it cannot read as
-    // empty. The reducer gathers WAVES splits per round, one per wave: once
-    // one word of the split has arrived it loads them all at once, re-reads
-    // the words still empty, marks every word empty again, and sums through
-    // LDS in split order, taking its own partial from registers at its place.
-    // The poll is bounded: after kPollLimit rounds the missing words count as
-    // NaN, so a launch always ends (and a lost partial shows in the output).
+    // accesses on this multi-XCD part, and exit. The reducer gathers WAVES
+    // splits per round, one per wave: once one word of the split has arrived
+    // it loads them all at once, re-reads the words still empty, marks every
+    // word empty again, and sums through LDS in split order, taking its own
+    // partial from registers at its place. The poll is bounded: after
+    // kPollLimit rounds the missing words count as NaN, so a launch always
+    // ends (and a lost partial shows in the output).
     constexpr int EPT = (ELEMS + NTHR - 1) / NTHR;  // output elements per thread
-    constexpr uint64_t kEmpty = ~0ull;
-    constexpr int kPollLimit = 1 << 18;
+    constexpr uint64_t kEmpty = ~0ull;              // two empty words
     uint64_t *wsw = a.pws + (size_t)tile * a.ksplit * ELEMS * 2;
     if (ks != rs) {
         for (int e = threadIdx.x; e < ELEMS; e += NTHR) {
-            u32x4 u = __builtin_bit_cast(u32x4, wave_sum(e));
-            u.x = u.x == 0xffffffffu ? 0x7fc00000u : u.x;
-            u.y = u.y == 0xffffffffu ? 0x7fc00000u : u.y;
-            u.z = u.z == 0xffffffffu ? 0x7fc00000u : u.z;
-            u.w = u.w == 0xffffffffu ? 0x7fc00000u : u.w;
+            const u32x4 u = publishable(__builtin_bit_cast(u32x4, wave_sum(e)));
             uint64_t *d = wsw + ((size_t)ks * ELEMS + e) * 2;
             __hip_atomic_store(d, (uint64_t)u.x | ((uint64_t)u.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(d + 1, (uint64_t)u.z | ((uint64_t)u.w << 32), __ATOMIC_RELAXED,
