@@ -331,12 +331,29 @@ PROFILE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv 
                "-o bench -- python3 -u $REPO/bench.py --no-cpu-baseline")
 PMC_CMDS = (
     "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o fetch "
-    "-- python3 $REPO/bench.py --pmc-pass",
+    "-- python3 $REPO/bench.py --pmc-pass > $REPO/gpurun_out/pmc_fetch.log 2>&1",
     "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o write "
-    "-- python3 $REPO/bench.py --pmc-pass",
+    "-- python3 $REPO/bench.py --pmc-pass > $REPO/gpurun_out/pmc_write.log 2>&1",
     "cd /tmp && rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d $REPO/gpurun_out/pmc_mfma "
-    "-o mfma -- python3 $REPO/bench.py --pmc-pass",
+    "-o mfma -- python3 $REPO/bench.py --pmc-pass > $REPO/gpurun_out/pmc_mfma.log 2>&1",
 )
+PMC_HASH_TAG = "pmc pass kernel sources:"
+
+
+def pass_source_hash(logs):
+    """The kernel-source hash the counter passes printed (every log must name
+    the same one): the counters belong to the sources that ran on the GPU, not
+    to whatever the tree holds when the summary is rendered."""
+    seen = set()
+    for path in logs:
+        with open(path) as f:
+            tags = [l.split(PMC_HASH_TAG, 1)[1].strip() for l in f if PMC_HASH_TAG in l]
+        if len(tags) != 1:
+            raise SystemExit("%s: expected one '%s' line, found %d" % (path, PMC_HASH_TAG, len(tags)))
+        seen.add(tags[0])
+    if len(seen) != 1:
+        raise SystemExit("the counter passes ran different kernel sources: %s" % sorted(seen))
+    return seen.pop()
 
 
 def md_decode1_trace(tr, trace_csv, bench_line=None, steps=50, warmup=5):
@@ -393,12 +410,13 @@ def md_loads_trace(lt, trace_csv):
     return "\n".join(L)
 
 
-def md_pmc(pm, csvs):
+def md_pmc(pm, csvs, logs):
     """profiles/pmc_loads.md from summarize_pmc()'s result."""
+    args = "%s --pmc-logs %s" % (" ".join(csvs), " ".join(logs))
     L = ["# HBM traffic and MFMA use per launch, every load: rocprofv3 --pmc (MI355X, 1 GPU)", "",
          "Commands (repo root on the GPU box; one counter set per run):", "", "```"] + list(PMC_CMDS) + [
-         "python bench.py --summarize-pmc %s > profiles/pmc_loads.json" % " ".join(csvs),
-         "python bench.py --summarize-pmc %s --md > profiles/pmc_loads.md" % " ".join(csvs), "```", "",
+         "python bench.py --summarize-pmc %s > profiles/pmc_loads.json" % args,
+         "python bench.py --summarize-pmc %s --md > profiles/pmc_loads.md" % args, "```", "",
          "The pass runs every load's five kernels cold (1 GiB flush before each), %d times, then copies 64 MiB three"
          % PMC_REPS,
          "times. FETCH_SIZE reads %.4f x fewer KiB than that copy moves and WRITE_SIZE reads it with scale %.4f; both"
@@ -417,8 +435,8 @@ def md_pmc(pm, csvs):
             e["load"], key.split("@")[0], e["kernel"], e["fetch_bytes"], e["write_bytes"], e["algorithmic_bytes"],
             (e["fetch_bytes"] + e["write_bytes"]) / e["algorithmic_bytes"], e.get("mfma_util_pct", "-"),
             e.get("mfma_mops_bf16", "-")))
-    L += ["", "Source hash of the kernels these counters belong to: `%s` (bench.py reports `traffic` = null once the "
-          "sources differ)." % pm["source_hash"], ""]
+    L += ["", "Source hash of the kernels these counters belong to, as printed by the passes themselves: `%s` "
+          "(bench.py reports `traffic` = null once the sources differ)." % pm["source_hash"], ""]
     return "\n".join(L)
 
 
@@ -432,7 +450,7 @@ def pmc_sequence():
     return [(name, l) for _ in range(PMC_REPS) for name in LOAD_ORDER for l in LAYERS]
 
 
-def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20):
+def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20, sources=None):
     """HBM bytes (and MFMA use) per launch of every (load, layer) from the counter
     passes of `bench.py --pmc-pass`.
 
@@ -440,12 +458,13 @@ def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20):
     of known size in the same pass (copy_bytes read and copy_bytes written).
     The optional third pass holds MfmaUtil (MFMA-busy cycles over all SIMD
     cycles of the dispatch, percent) and SQ_INSTS_VALU_MFMA_MOPS_BF16.
+    `sources`: the kernel-source hash the passes ran (pass_source_hash).
     """
     from gemv_decode_projections_amd import roofline as rf
     from workload import LOADS
 
     seq = pmc_sequence()
-    res = {"source_hash": source_hash(), "copy_bytes": copy_bytes, "launches": {}}
+    res = {"source_hash": sources, "copy_bytes": copy_bytes, "launches": {}}
 
     def launches(path, cname):
         rows = sorted((r for r in _read_csv(path) if r["Counter_Name"] == cname),
@@ -492,6 +511,7 @@ def pmc_pass():
 
     from gemv_decode_projections_amd import binding as B
 
+    print(PMC_HASH_TAG, source_hash(), flush=True)
     b = Bench()
     n = 64 << 20
     src = torch.ones(n, dtype=torch.uint8, device=b.dev)
@@ -524,6 +544,8 @@ def main():
                     help="print per-(load, layer) kernel durations from a rocprofv3 trace of bench.py")
     ap.add_argument("--md", action="store_true", help="with --summarize-*: print the profiles/ Markdown page")
     ap.add_argument("--bench-json", metavar="PATH", help="with --summarize-trace --md: the bench line of the same run")
+    ap.add_argument("--pmc-logs", nargs="+", metavar="LOG",
+                    help="with --summarize-pmc: the passes' output (names the kernel sources they ran)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="print HBM bytes per launch from the --pmc passes: FETCH_SIZE csv, WRITE_SIZE csv "
                          "and optionally the MfmaUtil csv")
@@ -548,8 +570,10 @@ def main():
     if args.summarize_pmc:
         if len(args.summarize_pmc) not in (2, 3):
             raise SystemExit("--summarize-pmc takes FETCH_CSV WRITE_CSV [MFMA_CSV]")
-        pm = summarize_pmc(*args.summarize_pmc)
-        print(md_pmc(pm, args.summarize_pmc) if args.md else json.dumps(pm, indent=1))
+        if not args.pmc_logs:
+            raise SystemExit("--summarize-pmc needs --pmc-logs (the passes' output, which names their sources)")
+        pm = summarize_pmc(*args.summarize_pmc, sources=pass_source_hash(args.pmc_logs))
+        print(md_pmc(pm, args.summarize_pmc, args.pmc_logs) if args.md else json.dumps(pm, indent=1))
         return
 
     if args.gpus != 1:

@@ -58,7 +58,8 @@ def test_pmc_summary_scales_by_the_copy_and_keys_every_shape(tmp_path):
     _pmc_csv(tmp_path / "w.csv", ["WRITE_SIZE"], lambda n, l, c: 8.0, 64 << 10)
     _pmc_csv(tmp_path / "m.csv", ["MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_BF16"],
              lambda n, l, c: 12.5 if c == "MfmaUtil" else LOADS[n])
-    r = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "m.csv"))
+    r = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "m.csv"),
+                            sources="abc")
     assert r["fetch_scale"] == pytest.approx(2.0) and r["write_scale"] == pytest.approx(1.0)
     assert len(r["launches"]) == len(LOADS) * len(LAYERS)
     for name, m in LOADS.items():
@@ -69,7 +70,20 @@ def test_pmc_summary_scales_by_the_copy_and_keys_every_shape(tmp_path):
             assert e["write_bytes"] == 8192
             assert e["algorithmic_bytes"] == rf.bytes_of(layer, m)
             assert e["mfma_util_pct"] == 12.5 and e["mfma_mops_bf16"] == m
-    assert r["source_hash"] == bench.source_hash()
+    assert r["source_hash"] == "abc"
+
+
+def test_pmc_summary_takes_the_source_hash_from_the_passes(tmp_path):
+    """The hash comes from what the counter passes printed, so counters taken
+    with other sources than the tree's are never labelled as current."""
+    for i, h in enumerate(("aaa", "aaa", "bbb")):
+        (tmp_path / ("p%d.log" % i)).write_text("noise\n%s %s\nmore\n" % (bench.PMC_HASH_TAG, h))
+    assert bench.pass_source_hash([str(tmp_path / "p0.log"), str(tmp_path / "p1.log")]) == "aaa"
+    with pytest.raises(SystemExit):
+        bench.pass_source_hash([str(tmp_path / "p0.log"), str(tmp_path / "p2.log")])
+    (tmp_path / "none.log").write_text("no tag\n")
+    with pytest.raises(SystemExit):
+        bench.pass_source_hash([str(tmp_path / "none.log")])
 
 
 def test_pmc_summary_refuses_a_pass_with_missing_launches(tmp_path):
@@ -115,7 +129,7 @@ def test_profile_pages_render(tmp_path):
     _pmc_csv(tmp_path / "f.csv", ["FETCH_SIZE"], lambda n, l, c: rf.bytes_of(l, LOADS[n]) / 2048.0, copy_kib)
     _pmc_csv(tmp_path / "w.csv", ["WRITE_SIZE"], lambda n, l, c: 8.0, 64 << 10)
     pm = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
-    page = bench.md_pmc(pm, ["f.csv", "w.csv"])
+    page = bench.md_pmc(pm, ["f.csv", "w.csv"], ["f.log", "w.log"])
     assert page.count("\n| ") >= len(LOADS) * len(LAYERS) and "rocprofv3 --pmc FETCH_SIZE" in page
     tr = {l: {"kernel": "skinny_kernel<1, 1, 8, 32, false, false>", "grid": 64, "n": 3, "mean_us": 5.0,
               "median_us": 5.0} for l in LAYERS}
