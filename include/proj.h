@@ -160,8 +160,11 @@ int proj_last_hip_error(void);
  *             multiple of it; kind 3: 4, 8 or 16, any split);
  *             k chunks of 2048 per row (kind 2: K = 2048 * spw)
  *   ksplit    workgroups that split K for one tile (1 = no cross-workgroup
- *             reduction; >1 = last-arriving workgroup sums the partials in
- *             split order)
+ *             reduction; >1 = one workgroup sums the partials in split order:
+ *             kinds 1 and 3 the last to arrive, counted with an atomic;
+ *             kind 0 the one the hardware dispatches last, which polls the
+ *             others' partials (a bounded wait: after 2^18 polls missing
+ *             words read as NaN, so a launch always ends))
  *   flags     bit 0 set: workgroup i keeps tile i. Clear (default): when the
  *             grid is a multiple of 8, consecutive tiles are grouped on one
  *             XCD (workgroups are dealt to the 8 XCDs round-robin).
@@ -186,7 +189,8 @@ typedef struct {
     int waves;
     int spw;
     int ksplit;
-    int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping); bit 2: 12-bit weights */
+    int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping); bit 2: 12-bit weights;
+                      bit 3: stream mode (kind 3) */
     int grid;      /* filled by proj_plan: workgroups launched */
     int block;     /* filled by proj_plan: threads per workgroup */
 } proj_config;
