@@ -104,7 +104,12 @@ __device__ __forceinline__ void split3_f32(const u32x4 &w0, const u32x4 &w1, u32
 // only publish and exit, so no arrival counter, store acknowledgement or
 // cache flush is needed.
 constexpr uint32_t kEmptyWord = 0xffffffffu;
-constexpr int kPollLimit = 1 << 18;   // polls before a reducer gives up (missing words read as NaN)
+// A reducer gives up after kPollLimit polls of a word (about a quarter of a
+// second): the missing words then read as NaN, so a launch always ends and a
+// lost partial shows in the output. Only a split held off the chip for that
+// long could publish after its reducer gave up, leaving words that a later
+// launch on the same layer would read as arrived.
+constexpr int kPollLimit = 1 << 18;
 
 // The one NaN pattern that equals the mark is published as the default NaN.
 __device__ __forceinline__ uint32_t publishable(uint32_t u) { return u == kEmptyWord ? 0x7fc00000u : u; }
