@@ -124,7 +124,7 @@ __device__ __forceinline__ u32x4 publishable(u32x4 u)
 // placed on the chip before it and finishes without waiting itself. With the
 // XCD remap (G % 8 == 0) logical id l runs on hardware id
 // 8 * (l % (G / 8)) + l / (G / 8); the walk uses one division.
-__device__ __forceinline__ int reducing_split(int l0, int stride, int n, int G, bool remap)
+__host__ __device__ __forceinline__ int reducing_split(int l0, int stride, int n, int G, bool remap)
 {
     if (!remap)
         return n - 1;
