@@ -111,11 +111,11 @@ const TiledVariant *find_tiled(int bmb, int bnb, int waves, int depth, int f32w)
     return nullptr;
 }
 
-const WideVariant *find_wide(int bmb, int bnb, int depth, int f32w)
+const WideVariant *find_wide(int bmb, int bnb, int depth, int f32w, int waves)
 {
     for (int i = 0; i < kWideVariantCount; ++i) {
         const WideVariant &v = kWideVariants[i];
-        if (v.bmb == bmb && v.bnb == bnb && v.depth == depth && v.f32w == f32w)
+        if (v.bmb == bmb && v.bnb == bnb && v.depth == depth && v.f32w == f32w && v.waves == waves)
             return &v;
     }
     return nullptr;
@@ -261,12 +261,12 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         return PROJ_OK;
     }
     if (c.kind == 3) {
-        // rb = 16-row blocks per tile (4 waves x rb/4), nt = 16-token blocks,
+        // rb = 16-row blocks per tile (waves x rb/waves, 4 or 8 waves), nt = 16-token blocks,
         // spw = weight prefetch depth in k-steps; K split unevenly in
         // super-steps of 2 (4 at depth 16) k-steps. flags bit 3: stream mode,
         // ksplit = number of workgroups sharing all tiles' super-steps.
-        const WideVariant *v = find_wide(c.rb, c.nt, c.spw, f32w);
-        if (!v || c.waves != 4)
+        const WideVariant *v = find_wide(c.rb, c.nt, c.spw, f32w, c.waves);
+        if (!v)
             return PROJ_ERR_UNSUPPORTED;
         if (ne % (kRowsPerBlock * c.rb) != 0 || c.ksplit < 1)
             return PROJ_ERR_UNSUPPORTED;
@@ -306,7 +306,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         L.fn = stream ? v->fn_stream : v->fn;
         L.kind = 3;
         L.grid = (int)grid;
-        L.block = 4 * kWave;
+        L.block = c.waves * kWave;
         WideArgs &A = L.wargs;
         A.wp = st.wp;
         A.zrow = st.zrow;
@@ -447,8 +447,30 @@ proj_config plan_default(int layer, int m)
         /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 16, 0}, {3, 8, 4, 16, 0}},
         /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 16, 0}, {3, 8, 4, 16, 0}},
     };
-    const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : (m <= 256 ? 2 : 3))];
     const int ne = n_eff_of(layer, m);
+    // Past 256 tokens: 256-row x 64-token tiles on the 8-wave wide kernel
+    // (two waves per SIMD, each with 32 rows) while the layer has at most 384
+    // such tiles (256 for o), split as below. Measured against the 4-wave
+    // rule that follows: qkv_gate m = 300 / 512 / 700 / 1000 30.9 / 36.8 /
+    // 57.0 / 60.8 -> 25.6 / 30.0 / 39.9 / 57.6 us, pooler m = 300 / 700 34.7 /
+    // 61.6 -> 29.7 / 56.0, unpooler m = 300 / 700 32.1 / 65.2 -> 29.7 / 61.2,
+    // o m = 300 12.2 -> 11.4; past those tile counts the 4-wave tiles won.
+    if (m > 256 && ne % 256 == 0) {
+        const long t16 = (long)(ne / 256) * ((m + 63) / 64);
+        if (t16 <= (layer == PROJ_O ? 256 : 384)) {
+            c.kind = 3;
+            c.rb = 16;
+            c.nt = 4;
+            c.waves = 8;
+            c.spw = 8;
+            int ks = (int)std::max(1L, std::min(4L, 256 / t16));
+            while (ks > 1 && (t16 * ks > 768 || t16 * ks * c.rb * c.nt * 1024 > (long)kWsBytes))
+                --ks;
+            c.ksplit = ks;
+            return c;
+        }
+    }
+    const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : (m <= 256 ? 2 : 3))];
     c.kind = e.kind;
     c.rb = e.rb;
     c.nt = e.nt;
@@ -788,10 +810,10 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
             c.kind = 3;
             c.nt = w.bnb;
             c.rb = w.bmb;
-            c.waves = 4;
+            c.waves = w.waves;
             c.spw = w.depth;
             c.ksplit = 1;
-            c.block = 4 * kWave;
+            c.block = w.waves * kWave;
             *cfg = c;
         }
         return PROJ_OK;

@@ -43,6 +43,7 @@ struct WideVariant {
     int bnb;
     int depth;        // weight prefetch distance in k-steps
     int f32w;
+    int waves;        // 4 or 8
     const void *fn;          // __global__ void (WideArgs): one tile per workgroup
     const void *fn_stream;   // the same kernel in stream mode
 };

@@ -90,11 +90,14 @@ constexpr int kCoherent = 16;
 constexpr int wide_superstep(int depth) { return depth >= 16 ? 4 : 2; }
 
 // STREAM: stream mode (a separate instantiation, so that the one-tile path
-// keeps its register allocation and schedule).
-template <int RBW, int BNB, int D, int S, bool F32W, bool STREAM>
-__global__ __launch_bounds__(256) void wide_kernel(WideArgs a)
+// keeps its register allocation and schedule). WAVES: 4, one per SIMD, or 8
+// (two per SIMD, each with half the rows: the same tile with half the
+// registers per wave, so one wave's memory waits can hide behind the other's
+// work).
+template <int RBW, int BNB, int D, int S, bool F32W, bool STREAM, int WAVES = 4>
+__global__ __launch_bounds__(WAVES * kWave) void wide_kernel(WideArgs a)
 {
-    constexpr int WAVES = 4;
+    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
     constexpr int NTHR = WAVES * kWave;
     constexpr int AW = F32W ? 2 : 1;                  // 1 KB units per weight fragment
     constexpr int BMB = WAVES * RBW;                  // row blocks per tile

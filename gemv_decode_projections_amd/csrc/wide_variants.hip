@@ -8,9 +8,11 @@
 
 namespace gdp {
 
-#define GDP_WIDE(RBW, BNB, D, F)                                                                       \
-    {RBW * 4, BNB, D, F, reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0), false>), \
-     reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0), true>)},
+#define GDP_WIDE_W(RBW, BNB, D, F, W)                                                                  \
+    {RBW * W, BNB, D, F, W,                                                                            \
+     reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0), false, W>), \
+     reinterpret_cast<const void *>(&wide_kernel<RBW, BNB, D, wide_superstep(D), (F != 0), true, W>)},
+#define GDP_WIDE(RBW, BNB, D, F) GDP_WIDE_W(RBW, BNB, D, F, 4)
 
 const WideVariant kWideVariants[] = {
     GDP_WIDE(1, 2, 8, 0)
@@ -28,6 +30,11 @@ const WideVariant kWideVariants[] = {
     GDP_WIDE(1, 2, 8, 1)
     GDP_WIDE(1, 4, 4, 1)
     GDP_WIDE(1, 8, 4, 1)
+    GDP_WIDE_W(1, 4, 8, 0, 8)
+    GDP_WIDE_W(1, 4, 16, 0, 8)
+    GDP_WIDE_W(1, 4, 4, 0, 8)
+    GDP_WIDE_W(1, 8, 8, 0, 8)
+    GDP_WIDE_W(2, 4, 8, 0, 8)
 };
 const int kWideVariantCount = sizeof(kWideVariants) / sizeof(kWideVariants[0]);
 

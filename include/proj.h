@@ -148,13 +148,14 @@ int proj_last_hip_error(void);
  *               kernel (m <= 8, router and the unpooler's 1024-row slice
  *               only: whole rows per workgroup from a row-major weight copy,
  *               FP32 multiply-adds), 3 = wide-tile MFMA kernel (large m;
- *               4 waves, up to 128 x 128 tiles, K split unevenly over up to
+ *               4 or 8 waves, up to 128 x 128 tiles, K split unevenly over up to
  *               KS/2 workgroups, KS/4 at prefetch depth 16)
  *   nt        token sub-tiles of 16 per workgroup (kinds 0, 1, 3); largest token
  *             count of the variant (kind 2)
  *   rb        16-row blocks per workgroup (kinds 0, 1, 3; a multiple of 4
  *             for kind 3); rows per workgroup (kind 2)
- *   waves     wavefronts per workgroup (4 for kinds 2 and 3)
+ *   waves     wavefronts per workgroup (4 for kind 2; 4 or 8 for kind 3, as
+ *             compiled: 8 waves hold the same tile with half the rows per wave)
  *   spw       k-steps of 32 per wave (kind 0); weight prefetch distance in
  *             k-steps (kind 1: the k-steps of one workgroup must be a
  *             multiple of it; kind 3: 4, 8 or 16, any split);

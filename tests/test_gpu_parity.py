@@ -139,9 +139,9 @@ def _variant_cases():
                 cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 2, 1))  # split groups across XCDs
                 break
             elif cfg.kind == 3 and n % (16 * cfg.rb) == 0:
-                cases.append((layer, 3, cfg.nt, cfg.rb, 4, cfg.spw, 1, 0))
-                cases.append((layer, 3, cfg.nt, cfg.rb, 4, cfg.spw, 3, 0))   # uneven split lengths
-                cases.append((layer, 3, cfg.nt, cfg.rb, 4, cfg.spw, 5, 1))   # uneven, groups across XCDs
+                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 1, 0))
+                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 3, 0))   # uneven split lengths
+                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 5, 1))   # uneven, across XCDs
                 break
     return cases
 
