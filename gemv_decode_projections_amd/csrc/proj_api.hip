@@ -448,23 +448,37 @@ proj_config plan_default(int layer, int m)
         /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 16, 0}, {3, 8, 4, 16, 0}},
     };
     const int ne = n_eff_of(layer, m);
-    // Past 256 tokens: 256-row x 64-token tiles on the 8-wave wide kernel
-    // (two waves per SIMD, each with 32 rows) while the layer has at most 384
-    // such tiles (256 for o), split as below. Measured against the 4-wave
-    // rule that follows: qkv_gate m = 300 / 512 / 700 / 1000 30.9 / 36.8 /
-    // 57.0 / 60.8 -> 25.6 / 30.0 / 39.9 / 57.6 us, pooler m = 300 / 700 34.7 /
-    // 61.6 -> 29.7 / 56.0, unpooler m = 300 / 700 32.1 / 65.2 -> 29.7 / 61.2,
-    // o m = 300 12.2 -> 11.4; past those tile counts the 4-wave tiles won.
+    // Past 256 tokens the 8-wave wide kernel (two waves per SIMD) holds
+    // 256-row tiles: 64 tokens wide while that still gives at least 160
+    // workgroups (with the split rule below), else 128 tokens wide while the
+    // grid stays within 512 workgroups (256 for o); past that the 4-wave
+    // rule further down. Measured against the 4-wave rule (us): qkv_gate
+    // m = 300 / 512 / 700 / 1000 / 2048 30.9 / 36.8 / 57.0 / 60.8 / 120.2 ->
+    // 25.6 / 30.0 / 39.9 / 47.3 / 84.8; pooler m = 300 / 700 / 2048 34.7 / 61.6 /
+    // 128.5 -> 29.7 / 56.0 / 109.2; unpooler m = 300 / 700 / 1000 / 2048 32.1 /
+    // 65.2 / 67.4 / 136.9 -> 29.7 / 47.9 / 57.9 / 114.0; o m = 300 / 700 / 1000
+    // 12.2 / 20.5 / 21.9 -> 11.4 / 18.5 / 20.9.
     if (m > 256 && ne % 256 == 0) {
-        const long t16 = (long)(ne / 256) * ((m + 63) / 64);
-        if (t16 <= (layer == PROJ_O ? 256 : 384)) {
+        auto split_for = [](long tiles) { return (int)std::max(1L, std::min(4L, 256 / tiles)); };
+        const long t64 = (long)(ne / 256) * ((m + 63) / 64);
+        const long t128 = (long)(ne / 256) * ((m + 127) / 128);
+        int nt = 0;
+        long tiles = 0;
+        if (t64 <= 256 && t64 * split_for(t64) >= 160) {
+            nt = 4;
+            tiles = t64;
+        } else if (t128 * split_for(t128) <= (layer == PROJ_O ? 256 : 512)) {
+            nt = 8;
+            tiles = t128;
+        }
+        if (nt) {
             c.kind = 3;
             c.rb = 16;
-            c.nt = 4;
+            c.nt = nt;
             c.waves = 8;
             c.spw = 8;
-            int ks = (int)std::max(1L, std::min(4L, 256 / t16));
-            while (ks > 1 && (t16 * ks > 768 || t16 * ks * c.rb * c.nt * 1024 > (long)kWsBytes))
+            int ks = split_for(tiles);
+            while (ks > 1 && tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes)
                 --ks;
             c.ksplit = ks;
             return c;
