@@ -14,9 +14,10 @@
 // workgroup to finish.
 //
 // gfx950 design:
-//   * A workgroup (4 waves) owns 4*RBW 16-row blocks x BNB 16-token blocks
-//     and a range of k-steps. Wave w owns RBW row blocks and every token
-//     block, so each weight byte is loaded by exactly one wave.
+//   * A workgroup (4 waves, or 8: two per SIMD) owns WAVES*RBW 16-row blocks
+//     x BNB 16-token blocks and a range of k-steps. Wave w owns RBW row
+//     blocks and every token block, so each weight byte is loaded by exactly
+//     one wave.
 //   * Weights (the HBM stream) go straight into registers from the
 //     fragment-major packing (repack.h), each wave reading 1 KB contiguous
 //     per load, D k-steps ahead of use.

@@ -1,8 +1,8 @@
 // Wide-tile kernel variants: (row blocks per wave, token blocks, weight
-// prefetch depth D in k-steps, FP32 weights). A workgroup tile is
-// (64*RBW) x (16*BNB); activations move in super-steps of 2 k-steps, or of 4
-// with the depth-16 prefetch (the pipeline keeps at most 4 super-steps of
-// weights ahead).
+// prefetch depth D in k-steps, FP32 weights[, waves]). A workgroup tile is
+// (16*W*RBW) x (16*BNB) with W = 4 waves (8 for GDP_WIDE_W(..., 8)); activations
+// move in super-steps of 2 k-steps, or of 4 with the depth-16 prefetch (the
+// pipeline keeps at most 4 super-steps of weights ahead).
 #include "variants.h"
 #include "wide.h"
 
