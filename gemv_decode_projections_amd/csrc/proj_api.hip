@@ -458,6 +458,19 @@ proj_config plan_default(int layer, int m)
     // 128.5 -> 29.7 / 56.0 / 109.2; unpooler m = 300 / 700 / 1000 / 2048 32.1 /
     // 65.2 / 67.4 / 136.9 -> 29.7 / 47.9 / 57.9 / 114.0; o m = 300 / 700 / 1000
     // 12.2 / 20.5 / 21.9 -> 11.4 / 18.5 / 20.9.
+    // The pooler at 129-192 tokens: the same 256 x 64 tiles with 5 splits
+    // (240 workgroups) beat its 128 x 64 tiles with 2 (m = 130 / 160 / 192:
+    // 24.6 / 24.9 / 25.6 -> 23.6 / 24.2 / 24.3 us); the other layers, and the
+    // pooler at 193-256, measured no gain.
+    if (layer == PROJ_POOLER && m > 128 && m <= 192) {
+        c.kind = 3;
+        c.rb = 16;
+        c.nt = 4;
+        c.waves = 8;
+        c.spw = 8;
+        c.ksplit = 5;
+        return c;
+    }
     if (m > 256 && ne % 256 == 0) {
         auto split_for = [](long tiles) { return (int)std::max(1L, std::min(4L, 256 / tiles)); };
         const long t64 = (long)(ne / 256) * ((m + 63) / 64);
