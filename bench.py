@@ -327,15 +327,17 @@ def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps, awkwa
     return out
 
 
-PROFILE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench "
+CMD_VARS = "`$REPO`: the repository root on the MI355X host; `$OUT`: the directory the runs write to"
+BENCH_CMD = "python3 $REPO/bench.py > $OUT/bench.json"
+PROFILE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_bench "
                "-o bench -- python3 -u $REPO/bench.py --no-cpu-baseline")
 PMC_CMDS = (
-    "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o fetch "
-    "-- python3 $REPO/bench.py --pmc-pass > $REPO/gpurun_out/pmc_fetch.log 2>&1",
-    "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o write "
-    "-- python3 $REPO/bench.py --pmc-pass > $REPO/gpurun_out/pmc_write.log 2>&1",
-    "cd /tmp && rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d $REPO/gpurun_out/pmc_mfma "
-    "-o mfma -- python3 $REPO/bench.py --pmc-pass > $REPO/gpurun_out/pmc_mfma.log 2>&1",
+    "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o fetch "
+    "-- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_fetch.log 2>&1",
+    "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o write "
+    "-- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_write.log 2>&1",
+    "cd /tmp && rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d $OUT/pmc_mfma "
+    "-o mfma -- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_mfma.log 2>&1",
 )
 PMC_HASH_TAG = "pmc pass kernel sources:"
 
@@ -356,16 +358,26 @@ def pass_source_hash(logs):
     return seen.pop()
 
 
-def md_decode1_trace(tr, trace_csv, bench_line=None, steps=50, warmup=5):
+# With --out-root DIR, paths under DIR are shown as $OUT/... on the profile pages.
+OUT_ROOT = None
+
+
+def shown(path):
+    if OUT_ROOT and os.path.abspath(path).startswith(os.path.abspath(OUT_ROOT) + os.sep):
+        return "$OUT/" + os.path.relpath(path, OUT_ROOT)
+    return path
+
+
+def md_decode1_trace(tr, trace_csv, bench_line=None, steps=50, warmup=5, bench_json=None):
     """profiles/decode1_kernels_trace.md from summarize_trace()'s result (and,
     when given, the JSON line of the same bench run without the profiler)."""
     from gemv_decode_projections_amd import roofline as rf
 
     L = ["# Decode-1 kernels: rocprofv3 kernel trace of bench.py (MI355X, 1 GPU)", "",
-         "Commands (repo root on the GPU box; `$REPO` is its path):", "", "```", PROFILE_CMD,
-         "python bench.py --summarize-trace %s --md --bench-json gpurun_out/bench.json > profiles/decode1_kernels_trace.md"
-         % trace_csv,
-         "python bench.py --summarize-loads-trace %s --md > profiles/loads_kernels_trace.md" % trace_csv, "```", "",
+         "Commands (%s):" % CMD_VARS, "", "```", BENCH_CMD, PROFILE_CMD,
+         "python bench.py --summarize-trace %s --md --bench-json %s > profiles/decode1_kernels_trace.md"
+         % (shown(trace_csv), shown(bench_json or "$OUT/bench.json")),
+         "python bench.py --summarize-loads-trace %s --md > profiles/loads_kernels_trace.md" % shown(trace_csv), "```", "",
          "Timed region: the %d decode-1 steps after %d warmup steps (each call preceded by a 1 GiB flush)." % (steps, warmup),
          "Kernel durations are the trace's start/end stamps."]
     if bench_line:
@@ -395,7 +407,7 @@ def md_loads_trace(lt, trace_csv):
     """profiles/loads_kernels_trace.md from summarize_loads_trace()'s result."""
     L = ["# Every load's kernels: rocprofv3 kernel trace of bench.py (MI355X, 1 GPU)", "",
          "Same trace as `decode1_kernels_trace.md` (command there); table from",
-         "`python bench.py --summarize-loads-trace %s --md`." % trace_csv,
+         "`python bench.py --summarize-loads-trace %s --md`." % shown(trace_csv),
          "Every launch is cold (1 GiB flush before it). Launches are matched in order with the bench's launch",
          "sequence (`bench.call_sequence`); n counts the event-timed calls, the graph warm-up run and the replays;",
          "loads named m=<m> are the awkward token counts. TB/s and TFLOP/s use algorithmic bytes and FLOPs",
@@ -412,9 +424,9 @@ def md_loads_trace(lt, trace_csv):
 
 def md_pmc(pm, csvs, logs):
     """profiles/pmc_loads.md from summarize_pmc()'s result."""
-    args = "%s --pmc-logs %s" % (" ".join(csvs), " ".join(logs))
+    args = "%s --pmc-logs %s" % (" ".join(shown(c) for c in csvs), " ".join(shown(g) for g in logs))
     L = ["# HBM traffic and MFMA use per launch, every load: rocprofv3 --pmc (MI355X, 1 GPU)", "",
-         "Commands (repo root on the GPU box; one counter set per run):", "", "```"] + list(PMC_CMDS) + [
+         "Commands (%s; one counter set per run):" % CMD_VARS, "", "```"] + list(PMC_CMDS) + [
          "python bench.py --summarize-pmc %s > profiles/pmc_loads.json" % args,
          "python bench.py --summarize-pmc %s --md > profiles/pmc_loads.md" % args, "```", "",
          "The pass runs every load's five kernels cold (1 GiB flush before each), %d times, then copies 64 MiB three"
@@ -544,12 +556,15 @@ def main():
                     help="print per-(load, layer) kernel durations from a rocprofv3 trace of bench.py")
     ap.add_argument("--md", action="store_true", help="with --summarize-*: print the profiles/ Markdown page")
     ap.add_argument("--bench-json", metavar="PATH", help="with --summarize-trace --md: the bench line of the same run")
+    ap.add_argument("--out-root", metavar="DIR", help="with --md: show paths under DIR as $OUT/... (the runs' output directory)")
     ap.add_argument("--pmc-logs", nargs="+", metavar="LOG",
                     help="with --summarize-pmc: the passes' output (names the kernel sources they ran)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="print HBM bytes per launch from the --pmc passes: FETCH_SIZE csv, WRITE_SIZE csv "
                          "and optionally the MfmaUtil csv")
     args = ap.parse_args()
+    global OUT_ROOT
+    OUT_ROOT = args.out_root
 
     if args.summarize_trace:
         tr = summarize_trace(args.summarize_trace, args.steps, args.warmup)
@@ -558,7 +573,7 @@ def main():
             if args.bench_json:
                 with open(args.bench_json) as f:
                     line = json.loads(f.read().strip().splitlines()[-1])
-            print(md_decode1_trace(tr, args.summarize_trace, line, args.steps, args.warmup))
+            print(md_decode1_trace(tr, args.summarize_trace, line, args.steps, args.warmup, args.bench_json))
         else:
             print(json.dumps(tr, indent=1))
         return
@@ -577,7 +592,7 @@ def main():
         return
 
     if args.gpus != 1:
-        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
+        sys.exit("bench.py measures one GPU only: this library has no multi-GPU path "
                  "(the projections are already one GPU's shard); run with --gpus 1")
     if args.pmc_pass:
         pmc_pass()
