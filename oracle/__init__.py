@@ -54,6 +54,10 @@ def _load():
     lib.oracle_linear_bf16w.restype = None
     lib.oracle_linear_f32w.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.oracle_linear_f32w.restype = None
+    lib.oracle_magnitude_bf16w.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.oracle_magnitude_bf16w.restype = None
+    lib.oracle_magnitude_f32w.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.oracle_magnitude_f32w.restype = None
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     _lib = lib
@@ -83,6 +87,20 @@ def matmul_bits(x_bits, w, n_rows=None):
     x_bits: uint16 (m x K) BF16 bit patterns. w: uint16 (BF16 bits) or float32,
     shape (N x K). Returns float64 (m x n_rows).
     """
+    return _run("linear", x_bits, w, n_rows)
+
+
+def magnitude_bits(x_bits, w, n_rows=None):
+    """FP64 |x| @ |W[:n_rows]|^T: per output, the sum of its terms' magnitudes.
+
+    Same operands and shape as matmul_bits. An FP32 accumulation of the
+    products in any order differs from the exact sum by at most a small
+    multiple of this value, which the acceptance check uses per element.
+    """
+    return _run("magnitude", x_bits, w, n_rows)
+
+
+def _run(kind, x_bits, w, n_rows):
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     if x_bits.ndim != 2 or w.ndim != 2 or x_bits.shape[1] != w.shape[1]:
         raise ValueError("shape mismatch: x %s, W %s" % (x_bits.shape, w.shape))
@@ -96,29 +114,59 @@ def matmul_bits(x_bits, w, n_rows=None):
     lib = _load()
     if w.dtype == np.uint16:
         wc = np.ascontiguousarray(w)
-        lib.oracle_linear_bf16w(x_bits.ctypes.data, wc.ctypes.data, m, n_rows, k, out.ctypes.data)
+        fn = lib.oracle_linear_bf16w if kind == "linear" else lib.oracle_magnitude_bf16w
+        fn(x_bits.ctypes.data, wc.ctypes.data, m, n_rows, k, out.ctypes.data)
     elif w.dtype == np.float32:
         wc = np.ascontiguousarray(w)
-        lib.oracle_linear_f32w(x_bits.ctypes.data, wc.ctypes.data, m, n_rows, k, out.ctypes.data)
+        fn = lib.oracle_linear_f32w if kind == "linear" else lib.oracle_magnitude_f32w
+        fn(x_bits.ctypes.data, wc.ctypes.data, m, n_rows, k, out.ctypes.data)
     else:
         raise TypeError("W must be uint16 BF16 bits or float32, got %s" % w.dtype)
     return out
 
 
-def reference(layer, x_bits, w):
-    """FP64 reference output of `layer` for BF16 activations `x_bits` (m x K)."""
+def _check_layer_operands(layer, w):
     n, k, wdt = _LAYERS[layer]
     if w.shape != (n, k):
         raise ValueError("%s expects W %dx%d, got %s" % (layer, n, k, w.shape))
     if (wdt == "f32") != (w.dtype == np.float32):
         raise TypeError("%s expects %s weights" % (layer, wdt))
+
+
+def reference(layer, x_bits, w):
+    """FP64 reference output of `layer` for BF16 activations `x_bits` (m x K)."""
+    _check_layer_operands(layer, w)
     m = x_bits.shape[0]
     return matmul_bits(x_bits, w, out_cols(layer, m))
 
 
-def reference_rows(layer, x_bits, w, rows):
-    """FP64 reference for a subset of token rows (sampled parity at full size)."""
-    rows = np.asarray(rows, dtype=np.int64)
+def magnitude(layer, x_bits, w):
+    """Per output of `layer`, the FP64 sum of |x| * |w| over its terms (same shape as reference)."""
+    _check_layer_operands(layer, w)
     m = x_bits.shape[0]
-    n_cols = out_cols(layer, m)
-    return matmul_bits(np.ascontiguousarray(x_bits[rows]), w, n_cols)
+    return magnitude_bits(x_bits, w, out_cols(layer, m))
+
+
+def _rows_of(x_bits, rows):
+    rows = np.asarray(rows, dtype=np.int64)
+    if rows.ndim != 1:
+        raise ValueError("rows must be a 1-D index list")
+    m = x_bits.shape[0]
+    if rows.size and (rows.min() < 0 or rows.max() >= m):
+        raise IndexError("row index out of range 0..%d" % (m - 1))
+    return np.ascontiguousarray(x_bits[rows])
+
+
+def reference_rows(layer, x_bits, w, rows):
+    """FP64 reference for a subset of the token rows of an m-row call (sampled
+    parity at full size): row j of the result is token rows[j] of
+    reference(layer, x_bits, w). The column count follows the call's m, not
+    the number of sampled rows (the unpooler slice rule depends on m)."""
+    _check_layer_operands(layer, w)
+    return matmul_bits(_rows_of(x_bits, rows), w, out_cols(layer, x_bits.shape[0]))
+
+
+def magnitude_rows(layer, x_bits, w, rows):
+    """magnitude() for a subset of token rows, as reference_rows()."""
+    _check_layer_operands(layer, w)
+    return magnitude_bits(_rows_of(x_bits, rows), w, out_cols(layer, x_bits.shape[0]))

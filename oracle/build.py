@@ -17,7 +17,7 @@ def build(verbose=False):
     os.makedirs(OUT_DIR, exist_ok=True)
     tmp = LIB + ".tmp%d" % os.getpid()
     # No -ffast-math: the FP64 sums must stay in ascending k as written.
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", SRC, "-o", tmp]
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", SRC, "-lm", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -18,6 +18,7 @@
  * keeps its own ascending-k sum, so the thread count does not change a bit of
  * the result.
  */
+#include <math.h>
 #include <omp.h>
 #include <stdint.h>
 #include <string.h>
@@ -63,6 +64,49 @@ void oracle_linear_f32w(const uint16_t *x, const float *W, int64_t m, int64_t n_
         for (int64_t k = 0; k < K; ++k)
             acc += bf16_to_double(xr[k]) * (double)wr[k];
         out[i * n_rows + n] = acc;
+    }
+}
+
+/*
+ * Magnitude of each output's terms: mag[i][n] = sum over k of |x[i, k]| * |W[n, k]|,
+ * in FP64, ascending k, from the same exact decode. An FP32 accumulation of the
+ * terms in any order is off from the exact sum by at most a multiple of this
+ * value (the standard error bound of a floating-point sum), so it scales the
+ * per-element part of the acceptance check (notebook note "Numerical formats
+ * and error": BF16 operands, FP32 accumulation, an order that is free).
+ */
+void oracle_magnitude_bf16w(const uint16_t *x, const uint16_t *W, int64_t m, int64_t n_rows,
+                            int64_t K, double *mag)
+{
+    int64_t total = m * n_rows;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < total; ++t) {
+        int64_t i = t / n_rows;
+        int64_t n = t % n_rows;
+        const uint16_t *xr = x + i * K;
+        const uint16_t *wr = W + n * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += fabs(bf16_to_double(xr[k])) * fabs(bf16_to_double(wr[k]));
+        mag[i * n_rows + n] = acc;
+    }
+}
+
+/* Router form of oracle_magnitude_bf16w: FP32 weights. */
+void oracle_magnitude_f32w(const uint16_t *x, const float *W, int64_t m, int64_t n_rows,
+                           int64_t K, double *mag)
+{
+    int64_t total = m * n_rows;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < total; ++t) {
+        int64_t i = t / n_rows;
+        int64_t n = t % n_rows;
+        const uint16_t *xr = x + i * K;
+        const float *wr = W + n * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += fabs(bf16_to_double(xr[k])) * fabs((double)wr[k]);
+        mag[i * n_rows + n] = acc;
     }
 }
 

@@ -62,18 +62,26 @@ def run_layer(layer, x_bits, stream=None, cfg=None):
 
 
 def compare(layer, got, w, xs, rows=None):
-    """Check `got` against the oracle; `rows` restricts to sampled token rows."""
+    """Check `got` against the oracle with every rule of oracle.check (norms,
+    probe rows, per-element bound); `rows` restricts the comparison to sampled
+    token rows. Every output, sampled or not, must be finite."""
+    if not np.all(np.isfinite(got)):
+        bad = np.argwhere(~np.isfinite(got))
+        raise AssertionError("%s: %d non-finite outputs, first at %s" % (layer, len(bad), tuple(bad[0])))
+    K = w.shape[1]
     if rows is None:
         ref = oracle.reference(layer, xs.bits, w)
+        mag = oracle.magnitude(layer, xs.bits, w)
         probe_rows = xs.probe_rows
         g = got
     else:
         rows = np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
         ref = oracle.reference_rows(layer, xs.bits, w, rows)
+        mag = oracle.magnitude_rows(layer, xs.bits, w, rows)
         pos = {int(r): i for i, r in enumerate(rows)}
         probe_rows = [pos[r] for r in xs.probe_rows if r in pos]
         g = got[rows]
-    return check(layer, g, ref, probe_rows)
+    return check(layer, g, ref, probe_rows, mag=mag, K=K)
 
 
 def sample_rows(xs, m, n_random=16, seed=0):

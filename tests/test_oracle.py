@@ -203,3 +203,76 @@ def test_thread_count_does_not_change_bits(oracle_mod):
     finally:
         oracle.set_threads(nt)
     assert np.array_equal(one, oracle.matmul_bits(xb, wb))
+
+
+def test_magnitude_brute_force_exact(oracle_mod):
+    # Sum of |x| * |w| over k: with small integers times powers of two every term
+    # and every partial sum is exact in FP64, so the oracle must equal exact
+    # rational arithmetic bit for bit (BF16 and FP32 weights).
+    rng = np.random.default_rng(4321)
+    for trial in range(30):
+        m, n, k = (int(v) for v in rng.integers(1, 9, size=3))
+        xv = rng.integers(-8, 9, size=(m, k)) * (2.0 ** rng.integers(-6, 7, size=(m, k)))
+        wv = rng.integers(-8, 9, size=(n, k)) * (2.0 ** rng.integers(-6, 7, size=(n, k)))
+        for w in (_bits(wv), wv.astype(np.float32)):
+            got = oracle.magnitude_bits(_bits(xv), w)
+            for i in range(m):
+                for j in range(n):
+                    exact = sum(abs(Fraction(float(xv[i, q]))) * abs(Fraction(float(wv[j, q]))) for q in range(k))
+                    assert got[i, j] == float(exact), (trial, i, j)
+
+
+def test_magnitude_sign_cases(oracle_mod):
+    # All terms of one sign: the magnitude is |reference|; mixed signs: strictly
+    # larger. A magnitude that kept any sign (|x| * w, x * |w|) fails one of these.
+    rng = np.random.default_rng(17)
+    k = 300
+    xv = np.abs(rng.standard_normal((3, k), dtype=np.float32))
+    wv = np.abs(rng.standard_normal((5, k), dtype=np.float32))
+    xb, wb = bf16_bits_from_f32(xv), bf16_bits_from_f32(wv)
+    for sx, sw in ((1, 1), (-1, 1), (1, -1), (-1, -1)):
+        xs_b = bf16_bits_from_f32(sx * (xb.astype(np.uint32) << 16).view(np.float32))
+        ws_b = bf16_bits_from_f32(sw * (wb.astype(np.uint32) << 16).view(np.float32))
+        ref = oracle.matmul_bits(xs_b, ws_b)
+        mag = oracle.magnitude_bits(xs_b, ws_b)
+        assert np.allclose(mag, np.abs(ref), rtol=1e-13, atol=0)
+    mixed = bf16_bits_from_f32(rng.standard_normal((3, k), dtype=np.float32))
+    ref = oracle.matmul_bits(mixed, wb)
+    mag = oracle.magnitude_bits(mixed, wb)
+    assert np.all(mag > np.abs(ref))
+
+
+def test_magnitude_of_layer_matches_textbook(oracle_mod):
+    w = make_weight("router", seed=2)
+    xs = make_x("router", 3, seed=4, outliers=True)
+    got = oracle.magnitude("router", xs.bits, w)
+    want = np.abs(_torch_decode(xs.bits)) @ np.abs(w.astype(np.float64)).T
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("m,rows", [(12, [3, 0, 11, 3, 7]),      # unpooler past the slice, fewer rows than 9
+                                    (6, [5, 1, 1]),               # unpooler slice, duplicate rows
+                                    (40, [39, 2, 20, 2, 0, 38, 5, 6, 7, 8, 9])])
+def test_reference_rows_equals_reference_subset(oracle_mod, m, rows):
+    # Sampled parity checks row subsets of an m-token call: the column count
+    # follows m (unpooler: 1024 at m <= 8, 8192 above, whatever the sample
+    # size), and row j of the subset is token rows[j], in the given order.
+    w = make_weight("unpooler", seed=1)
+    xs = make_x("unpooler", m, seed=9, outliers=True)
+    full = oracle.reference("unpooler", xs.bits, w)
+    sub = oracle.reference_rows("unpooler", xs.bits, w, rows)
+    assert sub.shape == (len(rows), 1024 if m <= 8 else 8192)
+    assert np.array_equal(sub, full[rows])
+    fmag = oracle.magnitude("unpooler", xs.bits, w)
+    assert np.array_equal(oracle.magnitude_rows("unpooler", xs.bits, w, rows), fmag[rows])
+
+
+def test_reference_rows_rejects_bad_rows(oracle_mod):
+    w = make_weight("o", seed=0)
+    xs = make_x("o", 4, seed=1)
+    with pytest.raises(IndexError):
+        oracle.reference_rows("o", xs.bits, w, [0, 4])
+    with pytest.raises(IndexError):
+        oracle.reference_rows("o", xs.bits, w, [-1])
+    with pytest.raises(ValueError):
+        oracle.reference_rows("o", xs.bits, w, [[0, 1]])
