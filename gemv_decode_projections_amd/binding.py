@@ -25,7 +25,6 @@ STATUS = {
     -7: "PROJ_ERR_HIP",
     -8: "PROJ_ERR_DEVICE",
 }
-PROJ_MAX_M = 4096
 
 
 class ProjError(RuntimeError):
@@ -72,14 +71,17 @@ def _lib():
         "proj_layer_dims": ([i, ip, ip, ip, ip], i),
         "proj_release": ([i], i),
         "proj_compressed": ([i], i),
+        "proj_split_giveups": ([i, i], i),
         "proj_strerror": ([i], ctypes.c_char_p),
         "proj_last_hip_error": ([], i),
         "proj_plan": ([i, i, cp], i),
         "proj_run_config": ([i, vp, i, vp, vp, cp], i),
         "proj_num_variants": ([], i),
         "proj_variant": ([i, ip, cp], i),
-        "proj_bench_flush": ([vp, sz, vp, vp], i),
-        "proj_bench_read_floor": ([vp, sz, vp, vp, i, i, i, vp, vp], i),
+        "proj_bench_flush": ([vp, sz, vp, i, vp], i),
+        "proj_bench_read_floor": ([vp, sz, vp, vp, i, i, i, i, vp, vp], i),
+        "proj_bench_stamp": ([vp, i, vp], i),
+        "proj_bench_wallclock_khz": ([ip], i),
         "proj_run_timed": ([i, vp, i, vp, vp, cp, vp, vp], i),
         "proj_bench_event_create": ([ctypes.POINTER(vp)], i),
         "proj_bench_event_destroy": ([vp], i),
@@ -148,16 +150,56 @@ def proj_prepare(layer, W):
     _check(_lib().proj_prepare(lid, _ptr(W)), "proj_prepare(%s)" % _layers.layer_name(lid))
 
 
+_BF16_LIKE = ("torch.bfloat16", "torch.int16", "torch.uint16")
+
+
+def _check_io(layer, x, m, out):
+    """Host-side check of the tensors a launch will read and write: the C ABI
+    takes raw pointers, so a tensor of the wrong shape would become an
+    out-of-bounds GPU access. Raises ValueError before anything is launched."""
+    m = int(m)
+    if m < 1:
+        return    # the library reports PROJ_ERR_M
+    name = _layers.layer_name(layer)
+    _, k, _, ob = _layers.DIMS[name]
+    cols = _layers.n_eff(name, m)
+    for what, t, width, dtypes in (("x", x, k, _BF16_LIKE),
+                                   ("out", out, cols, ("torch.float32",) if ob == 4 else _BF16_LIKE)):
+        if t is None or not hasattr(t, "data_ptr"):
+            raise ValueError("%s(m=%d): %s must be a device tensor" % (name, m, what))
+        if str(t.dtype) not in dtypes:
+            raise ValueError("%s(m=%d): %s has dtype %s, expected one of %s" % (name, m, what, t.dtype, dtypes))
+        if t.dim() != 2 or t.shape[1] != width or t.shape[0] < m:
+            raise ValueError("%s(m=%d): %s has shape %s, expected (>= %d, %d)"
+                             % (name, m, what, tuple(t.shape), m, width))
+        if not t.is_contiguous():
+            raise ValueError("%s(m=%d): %s must be contiguous (row-major)" % (name, m, what))
+    for what, t in (("x", x), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError("%s(m=%d): %s is on %s, not a GPU" % (name, m, what, t.device))
+    if x.device != out.device:
+        raise ValueError("%s(m=%d): x on %s, out on %s" % (name, m, x.device, out.device))
+
+
 def proj_run(layer, x, m, out, stream=None):
     """out[:m] = x[:m] @ W^T, launched on `stream` (default: torch's current stream)."""
+    _check_io(layer, x, m, out)
     _check(_lib().proj_run(_layers.layer_id(layer), _ptr(x), int(m), _ptr(out), _stream(stream)),
            "proj_run(%s, m=%d)" % (_layers.layer_name(layer), m))
 
 
 def proj_run_config(layer, x, m, out, cfg, stream=None):
+    _check_io(layer, x, m, out)
     _check(_lib().proj_run_config(_layers.layer_id(layer), _ptr(x), int(m), _ptr(out), _stream(stream),
                                   ctypes.byref(cfg)),
            "proj_run_config(%s, m=%d, %s)" % (_layers.layer_name(layer), m, cfg.as_dict()))
+
+
+def proj_split_giveups(layer, reset=False):
+    """Give-ups of the layer's polled split-K reducers since prepare or the last
+    reset; reset=True also restores the workspace's empty marks (synchronizes)."""
+    rc = _lib().proj_split_giveups(_layers.layer_id(layer), 1 if reset else 0)
+    return _check(rc, "proj_split_giveups") if rc < 0 else rc
 
 
 def proj_compressed(layer):
@@ -189,16 +231,39 @@ def proj_variant(i):
     return bool(f32.value), cfg
 
 
-def proj_bench_flush(buf, sink, stream=None):
-    _check(_lib().proj_bench_flush(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
-                                   _stream(stream)), "proj_bench_flush")
+FLUSH_NT, FLUSH_PLAIN = 0, 1
 
 
-def proj_bench_read_floor(buf, nbytes, sink, grid=0, waves=0, unroll=4, stream=None, events=None):
+def proj_bench_flush(buf, sink, stream=None, mode=FLUSH_NT, nbytes=None):
+    """Read `nbytes` (default: all) of `buf`; mode FLUSH_NT (non-temporal) or FLUSH_PLAIN."""
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if n > buf.numel() * buf.element_size():
+        raise ValueError("flush of %d bytes from a %d-byte buffer" % (n, buf.numel() * buf.element_size()))
+    _check(_lib().proj_bench_flush(_ptr(buf), n, _ptr(sink), int(mode), _stream(stream)), "proj_bench_flush")
+
+
+def proj_bench_read_floor(buf, nbytes, sink, grid=0, waves=0, unroll=4, stream=None, events=None, mode=FLUSH_NT):
+    if int(nbytes) > buf.numel() * buf.element_size():
+        raise ValueError("read floor of %d bytes from a %d-byte buffer" % (nbytes, buf.numel() * buf.element_size()))
+    if sink.numel() * sink.element_size() < 4 * max(int(grid) or 1024, 4096):
+        raise ValueError("sink too small for grid %d" % grid)
     ev0, ev1 = (events.start, events.stop) if events is not None else (None, None)
     _check(_lib().proj_bench_read_floor(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream),
-                                        int(grid), int(waves), int(unroll), ev0, ev1),
+                                        int(grid), int(waves), int(unroll), int(mode), ev0, ev1),
            "proj_bench_read_floor")
+
+
+def proj_bench_stamp(buf, idx, stream=None):
+    """Write the GPU wall clock to buf[idx] (buf: int64 device tensor)."""
+    if not 0 <= int(idx) < buf.numel() or buf.element_size() != 8:
+        raise ValueError("stamp index %d outside a %d-word buffer" % (idx, buf.numel()))
+    _check(_lib().proj_bench_stamp(_ptr(buf), int(idx), _stream(stream)), "proj_bench_stamp")
+
+
+def proj_bench_wallclock_khz():
+    khz = ctypes.c_int()
+    _check(_lib().proj_bench_wallclock_khz(ctypes.byref(khz)), "proj_bench_wallclock_khz")
+    return khz.value
 
 
 class KernelTimer:
@@ -230,6 +295,7 @@ class KernelTimer:
 
 def proj_run_timed(layer, x, m, out, timer, cfg=None, stream=None):
     """proj_run / proj_run_config launched with `timer` bracketing the kernel itself."""
+    _check_io(layer, x, m, out)
     _check(_lib().proj_run_timed(_layers.layer_id(layer), _ptr(x), int(m), _ptr(out), _stream(stream),
                                  ctypes.byref(cfg) if cfg is not None else None, timer.start, timer.stop),
            "proj_run_timed(%s, m=%d)" % (_layers.layer_name(layer), m))

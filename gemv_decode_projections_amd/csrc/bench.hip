@@ -11,6 +11,18 @@ namespace {
 
 constexpr uint32_t kSinkMagic = 0x9e3779b9u;   // data-dependent store keeps reads live
 
+// One 16-byte load: non-temporal (NT) or plain (cached like the GEMV
+// kernels' weight stream).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4 *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void flush_kernel(const u32x4 *__restrict__ buf, size_t units,
                                                      uint32_t *__restrict__ sink)
 {
@@ -18,21 +30,21 @@ __global__ __launch_bounds__(256) void flush_kernel(const u32x4 *__restrict__ bu
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < units; i += 4 * stride) {
-        u32x4 a = __builtin_nontemporal_load(buf + i);
-        u32x4 b = __builtin_nontemporal_load(buf + i + stride);
-        u32x4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
-        u32x4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
+        u32x4 a = load16<NT>(buf + i);
+        u32x4 b = load16<NT>(buf + i + stride);
+        u32x4 c = load16<NT>(buf + i + 2 * stride);
+        u32x4 d = load16<NT>(buf + i + 3 * stride);
         acc ^= a.x ^ b.y ^ c.z ^ d.w;
     }
     for (; i < units; i += stride) {
-        u32x4 a = __builtin_nontemporal_load(buf + i);
+        u32x4 a = load16<NT>(buf + i);
         acc ^= a.x;
     }
     if (acc == kSinkMagic)
         sink[blockIdx.x] = acc;
 }
 
-template <int UNROLL>
+template <int UNROLL, bool NT>
 __global__ __launch_bounds__(1024) void read_floor_kernel(const u32x4 *__restrict__ buf, size_t units,
                                                            size_t per_wg, size_t per_wave,
                                                            uint32_t *__restrict__ sink)
@@ -49,15 +61,26 @@ __global__ __launch_bounds__(1024) void read_floor_kernel(const u32x4 *__restric
         u32x4 v[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            v[u] = __builtin_nontemporal_load(buf + i + u * kWave);
+            v[u] = load16<NT>(buf + i + u * kWave);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
             acc ^= v[u].x ^ v[u].w;
     }
     for (; i < end; i += kWave)
-        acc ^= __builtin_nontemporal_load(buf + i).y;
+        acc ^= load16<NT>(buf + i).y;
     if (acc == kSinkMagic)
         sink[blockIdx.x] = acc;
+}
+
+// One lane writes the GPU's constant-rate wall clock (s_memrealtime) to
+// out[idx]. Placed before and after a load's kernels inside a graph, two
+// stamps give the span of those kernels on the GPU, gaps between them
+// included, without the host's launch path.
+__global__ __launch_bounds__(64) void stamp_kernel(uint64_t *__restrict__ out, int idx)
+{
+    const uint64_t t = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0)
+        out[idx] = t;
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
@@ -100,19 +123,25 @@ using namespace gdp;
 
 extern "C" {
 
-int proj_bench_flush(const void *buf, size_t bytes, void *sink, void *stream)
+int proj_bench_flush(const void *buf, size_t bytes, void *sink, int mode, void *stream)
 {
     if (!buf || !sink)
         return PROJ_ERR_NULL;
     if (((uintptr_t)buf & 15u) || (bytes & 15u))
         return PROJ_ERR_ALIGN;
-    hipLaunchKernelGGL(flush_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const u32x4 *>(buf), bytes / 16, static_cast<uint32_t *>(sink));
+    if (mode != 0 && mode != 1)
+        return PROJ_ERR_UNSUPPORTED;
+    if (mode == 0)
+        hipLaunchKernelGGL(flush_kernel<true>, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const u32x4 *>(buf), bytes / 16, static_cast<uint32_t *>(sink));
+    else
+        hipLaunchKernelGGL(flush_kernel<false>, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const u32x4 *>(buf), bytes / 16, static_cast<uint32_t *>(sink));
     return hip_status(hipGetLastError());
 }
 
 int proj_bench_read_floor(const void *buf, size_t bytes, void *sink, void *stream, int grid, int waves,
-                          int unroll, void *ev_start, void *ev_stop)
+                          int unroll, int mode, void *ev_start, void *ev_stop)
 {
     if (!buf || !sink)
         return PROJ_ERR_NULL;
@@ -122,7 +151,7 @@ int proj_bench_read_floor(const void *buf, size_t bytes, void *sink, void *strea
         grid = 1024;
     if (waves <= 0)
         waves = 8;
-    if (waves > 16)
+    if (waves > 16 || (mode != 0 && mode != 1))
         return PROJ_ERR_UNSUPPORTED;
     const size_t units = bytes / 16;
     size_t per_wg = (units + grid - 1) / grid;
@@ -134,11 +163,15 @@ int proj_bench_read_floor(const void *buf, size_t bytes, void *sink, void *strea
     uint32_t *k = static_cast<uint32_t *>(sink);
     dim3 g(grid), blk(waves * kWave);
     const void *fn;
-    switch (unroll) {
-    case 1: fn = reinterpret_cast<const void *>(&read_floor_kernel<1>); break;
-    case 2: fn = reinterpret_cast<const void *>(&read_floor_kernel<2>); break;
-    case 4: fn = reinterpret_cast<const void *>(&read_floor_kernel<4>); break;
-    case 8: fn = reinterpret_cast<const void *>(&read_floor_kernel<8>); break;
+    switch (unroll * 2 + mode) {
+    case 2: fn = reinterpret_cast<const void *>(&read_floor_kernel<1, true>); break;
+    case 3: fn = reinterpret_cast<const void *>(&read_floor_kernel<1, false>); break;
+    case 4: fn = reinterpret_cast<const void *>(&read_floor_kernel<2, true>); break;
+    case 5: fn = reinterpret_cast<const void *>(&read_floor_kernel<2, false>); break;
+    case 8: fn = reinterpret_cast<const void *>(&read_floor_kernel<4, true>); break;
+    case 9: fn = reinterpret_cast<const void *>(&read_floor_kernel<4, false>); break;
+    case 16: fn = reinterpret_cast<const void *>(&read_floor_kernel<8, true>); break;
+    case 17: fn = reinterpret_cast<const void *>(&read_floor_kernel<8, false>); break;
     default: return PROJ_ERR_UNSUPPORTED;
     }
     void *params[] = {&b, const_cast<size_t *>(&units), &per_wg, &per_wave, &k};
@@ -187,6 +220,28 @@ int proj_bench_copy(const void *src, void *dst, size_t bytes, void *stream)
     hipLaunchKernelGGL(copy_kernel, dim3(2048), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), bytes / 16);
     return hip_status(hipGetLastError());
+}
+
+int proj_bench_stamp(void *buf, int idx, void *stream)
+{
+    if (!buf)
+        return PROJ_ERR_NULL;
+    if (((uintptr_t)buf & 7u) || idx < 0)
+        return PROJ_ERR_ALIGN;
+    hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint64_t *>(buf), idx);
+    return hip_status(hipGetLastError());
+}
+
+int proj_bench_wallclock_khz(int *khz)
+{
+    if (!khz)
+        return PROJ_ERR_NULL;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+    return hip_status(e);
 }
 
 int proj_bench_empty(void *stream)

@@ -106,9 +106,11 @@ __device__ __forceinline__ void split3_f32(const u32x4 &w0, const u32x4 &w1, u32
 constexpr uint32_t kEmptyWord = 0xffffffffu;
 // A reducer gives up after kPollLimit polls of a word (about a quarter of a
 // second): the missing words then read as NaN, so a launch always ends and a
-// lost partial shows in the output. Only a split held off the chip for that
+// lost partial shows in the output; the reducer also counts the give-up in a
+// per-layer word the host can read. Only a split held off the chip for that
 // long could publish after its reducer gave up, leaving words that a later
-// launch on the same layer would read as arrived.
+// launch on the same layer would read as arrived; the host's reset of the
+// count restores every mark.
 constexpr int kPollLimit = 1 << 18;
 
 // The one NaN pattern that equals the mark is published as the default NaN.

@@ -45,6 +45,16 @@ constexpr int kRowMajorRows[PROJ_NUM_LAYERS] = {0, 0, 0, kSliceRows, 256};
 
 constexpr size_t kWsBytes = 32u << 20;       // split-K partials per layer (each of the two workspaces)
 constexpr size_t kCounters = 1u << 16;       // split-K arrival counters per layer
+// Token counts scanned for the kernels the dispatch table can pick: past this
+// count every layer's plan is the same kernel with a larger grid.
+constexpr int kPlanScanM = 16384;
+// Largest token count: keeps every tile count and rounding in the planning
+// arithmetic inside int (x alone would then take 2 TB or more).
+constexpr int kMaxM = 1 << 30;
+// proj_config.flags bit 4 (skinny kernel, test only): the splits that do not
+// reduce drop their partials and the reducer polls once, so every reducer
+// gives up; a host-forced stand-in for a split that never arrives.
+constexpr int kFlagTestLostSplit = 16;
 
 struct LayerState {
     void *wp = nullptr;
@@ -59,6 +69,7 @@ struct LayerState {
     uint64_t *zexc = nullptr;     // corrections: N rows x zcr slots
     int zcr = -1;                 // slots per row; -1: no 12-bit form
     uint32_t zt0 = 0, zt1 = 0;    // exponent table
+    uint32_t *giveups = nullptr;  // polled split-K: reducer give-ups since prepare / last reset
     int device = -1;
     bool prepared = false;
 };
@@ -162,19 +173,19 @@ struct Launch {
     int block;
 };
 
-// Checks that `c` tiles (layer, m) exactly and fits the workspace; fills `L`.
-int resolve(int layer, int m, const proj_config &c, Launch &L)
+// Checks that `c` tiles (layer, m) exactly and fits the workspace of layer
+// state `st`; fills `L`.
+int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState &st)
 {
     const LayerInfo &li = kLayers[layer];
     const int f32w = li.w_bytes == 4 ? 1 : 0;
     const int KS = li.K / kStepK;
     const int ne = n_eff_of(layer, m);
-    const LayerState &st = g_layers[layer];
     if (c.ksplit < 1)
         return PROJ_ERR_UNSUPPORTED;
     // Flag bits each kind understands: 0 placement (all), 2 12-bit weights
-    // (kind 0), 3 stream mode (kind 3).
-    const int known = 1 | (c.kind == 0 ? 4 : 0) | (c.kind == 3 ? 8 : 0);
+    // (kind 0), 3 stream mode (kind 3), 4 the test-only lost split (kind 0).
+    const int known = 1 | (c.kind == 0 ? 4 | kFlagTestLostSplit : 0) | (c.kind == 3 ? 8 : 0);
     if (c.flags & ~known)
         return PROJ_ERR_UNSUPPORTED;
     if (c.kind == 0) {
@@ -218,6 +229,9 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
         A.n_tt = n_tt;
         A.ksplit = c.ksplit;
         A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
+        A.giveups = st.giveups;
+        A.drop_publish = (c.flags & kFlagTestLostSplit) ? 1 : 0;
+        A.poll_limit = A.drop_publish ? 1 : kPollLimit;
         return PROJ_OK;
     }
     if (c.kind == 1) {
@@ -350,7 +364,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L)
 // Buckets: m <= 8 (one 16-token tile, unpooler slice), 9..16, 17..32 (two
 // 16-token tiles), and m > 32. Entries are the fastest measured cold-cache
 // configurations on MI355X (kernel duration, plain weight loads).
-proj_config plan_default(int layer, int m)
+proj_config plan_default(int layer, int m, int zcr)
 {
     struct Entry {
         int nt, rb, waves, spw, ksplit, z;   // z: read the 12-bit weights when the layer has them
@@ -395,7 +409,7 @@ proj_config plan_default(int layer, int m)
         c.waves = e.waves;
         c.spw = e.spw;
         c.ksplit = e.ksplit;
-        c.flags = (e.z && g_layers[layer].zcr >= 0) ? 4 : 0;
+        c.flags = (e.z && zcr >= 0) ? 4 : 0;
         return c;
     }
     // The router past 32 tokens stays on the skinny kernel: with 16 row
@@ -411,13 +425,22 @@ proj_config plan_default(int layer, int m)
         c.waves = e.waves;
         c.spw = e.spw;
         c.ksplit = e.ksplit;
+        // Past 8192 tokens the split partials would overflow the workspace:
+        // the whole K range in one workgroup (16 waves of 16 k-steps).
+        const long long parts = (long long)(kLayers[layer].N / (16 * e.rb)) * ((m + 16 * e.nt - 1) / (16 * e.nt)) *
+                                e.ksplit * e.rb * e.nt * kWave * (long long)sizeof(f32x4);
+        if (parts > (long long)kWsBytes) {
+            c.waves = 16;
+            c.spw = 16;
+            c.ksplit = 1;
+        }
         return c;
     }
     // qkv_gate just past 32 tokens: the 12-bit skinny kernel over 16-token
     // tiles (each tile re-reads the 12-bit stream, mostly from L2) beat the
     // tiled kernels up to 48 tokens (m = 33 / 48: 12.4 / 12.7 us against
     // 13.4 / 13.5) and lost at 64 (17.2 against 13.3).
-    if (layer == PROJ_QKV_GATE && m <= 48 && g_layers[layer].zcr >= 0) {
+    if (layer == PROJ_QKV_GATE && m <= 48 && zcr >= 0) {
         c.nt = 1;
         c.rb = 2;
         c.waves = 8;
@@ -522,7 +545,7 @@ int check_run_args(int layer, const void *x, int m, void *out)
 {
     if (check_layer(layer))
         return PROJ_ERR_LAYER;
-    if (m < 1 || m > PROJ_MAX_M)
+    if (m < 1 || m > kMaxM)
         return PROJ_ERR_M;
     if (!x || !out)
         return PROJ_ERR_NULL;
@@ -644,7 +667,54 @@ void free_layer(LayerState &st)
         (void)hipFree(st.wz);
     if (st.zexc)
         (void)hipFree(st.zexc);
+    if (st.giveups)
+        (void)hipFree(st.giveups);
     st = LayerState{};
+}
+
+// Launches every kernel the dispatch table can pick for the layer once (guide
+// ch. 10 "Measure, experiment, and try your own changes", Experiment D: an
+// unsupported configuration shows up in prepare's warm-up, never in a timed
+// call). Every token count up to kPlanScanM is planned and resolved, so a
+// table entry that is not compiled, or that does not tile the layer, fails
+// prepare; each distinct kernel then runs once on zero activations, so its
+// code object and first-launch cost are paid here and not inside a caller's
+// graph capture or timed region.
+int warm_up(int layer, const LayerState &ns)
+{
+    const LayerInfo &li = kLayers[layer];
+    constexpr int kWarmM = kSliceMaxM + 1;          // past the unpooler slice
+    void *zx = nullptr, *out = nullptr;
+    hipError_t e;
+    if ((e = hipMalloc(&zx, (size_t)kWarmM * li.K * 2)) != hipSuccess ||
+        (e = hipMemset(zx, 0, (size_t)kWarmM * li.K * 2)) != hipSuccess ||
+        (e = hipMalloc(&out, (size_t)kWarmM * li.N * li.o_bytes)) != hipSuccess) {
+        (void)hipFree(zx);
+        return hip_fail(e);
+    }
+    std::vector<const void *> done;
+    int rc = PROJ_OK;
+    for (int m = 1; m <= kPlanScanM && rc == PROJ_OK; ++m) {
+        const proj_config c = plan_default(layer, m, ns.zcr);
+        Launch L;
+        if ((rc = resolve(layer, m, c, L, ns)) != PROJ_OK)
+            break;
+        if (std::find(done.begin(), done.end(), L.fn) != done.end())
+            continue;
+        done.push_back(L.fn);
+        // The same configuration over one token (rows of the slice) or, for
+        // the unpooler past its slice, over kWarmM tokens.
+        const int mw = (layer == PROJ_UNPOOLER && m > kSliceMaxM) ? kWarmM : 1;
+        Launch W;
+        if ((rc = resolve(layer, mw, c, W, ns)) != PROJ_OK)
+            break;
+        rc = launch(W, zx, out, nullptr);
+    }
+    if (rc == PROJ_OK && (e = hipDeviceSynchronize()) != hipSuccess)
+        rc = hip_fail(e);
+    (void)hipFree(zx);
+    (void)hipFree(out);
+    return rc;
 }
 
 }  // namespace
@@ -663,12 +733,12 @@ int proj_prepare(int layer, const void *W)
     if (!aligned16(W))
         return PROJ_ERR_ALIGN;
     const LayerInfo &li = kLayers[layer];
-    LayerState &st = g_layers[layer];
-    free_layer(st);
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return hip_fail(e);
+    // The new state is built, repacked and warmed up next to the old one,
+    // which stays usable until the new one is complete.
     const size_t wbytes = (size_t)li.N * li.K * li.w_bytes;
     LayerState ns;
     ns.device = dev;
@@ -678,6 +748,8 @@ int proj_prepare(int layer, const void *W)
         (e = hipMemset(ns.counters, 0, kCounters * sizeof(uint32_t))) != hipSuccess ||
         (e = hipMalloc(reinterpret_cast<void **>(&ns.pws), kWsBytes)) != hipSuccess ||
         (e = hipMemset(ns.pws, 0xff, kWsBytes)) != hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void **>(&ns.giveups), 64)) != hipSuccess ||
+        (e = hipMemset(ns.giveups, 0, 64)) != hipSuccess ||
         (e = hipMalloc(reinterpret_cast<void **>(&ns.zrow), (size_t)li.K * 2)) != hipSuccess ||
         (e = hipMemset(ns.zrow, 0, (size_t)li.K * 2)) != hipSuccess) {
         free_layer(ns);
@@ -710,8 +782,14 @@ int proj_prepare(int layer, const void *W)
         free_layer(ns);
         return hip_fail(e);
     }
+    const int rc = warm_up(layer, ns);
+    if (rc) {
+        free_layer(ns);
+        return rc;
+    }
     ns.prepared = true;
-    st = ns;
+    free_layer(g_layers[layer]);
+    g_layers[layer] = ns;
     return PROJ_OK;
 }
 
@@ -720,9 +798,9 @@ int proj_run(int layer, const void *x, int m, void *out, void *stream)
     int rc = check_run_args(layer, x, m, out);
     if (rc)
         return rc;
-    proj_config c = plan_default(layer, m);
+    proj_config c = plan_default(layer, m, g_layers[layer].zcr);
     Launch L;
-    rc = resolve(layer, m, c, L);
+    rc = resolve(layer, m, c, L, g_layers[layer]);
     if (rc)
         return rc;
     return launch(L, x, out, static_cast<hipStream_t>(stream));
@@ -736,7 +814,7 @@ int proj_run_config(int layer, const void *x, int m, void *out, void *stream, co
     if (!cfg)
         return PROJ_ERR_NULL;
     Launch L;
-    rc = resolve(layer, m, *cfg, L);
+    rc = resolve(layer, m, *cfg, L, g_layers[layer]);
     if (rc)
         return rc;
     return launch(L, x, out, static_cast<hipStream_t>(stream));
@@ -748,9 +826,9 @@ int proj_run_timed(int layer, const void *x, int m, void *out, void *stream, con
     int rc = check_run_args(layer, x, m, out);
     if (rc)
         return rc;
-    proj_config c = cfg ? *cfg : plan_default(layer, m);
+    proj_config c = cfg ? *cfg : plan_default(layer, m, g_layers[layer].zcr);
     Launch L;
-    rc = resolve(layer, m, c, L);
+    rc = resolve(layer, m, c, L, g_layers[layer]);
     if (rc)
         return rc;
     return launch(L, x, out, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
@@ -761,13 +839,13 @@ int proj_plan(int layer, int m, proj_config *cfg)
 {
     if (check_layer(layer))
         return PROJ_ERR_LAYER;
-    if (m < 1 || m > PROJ_MAX_M)
+    if (m < 1 || m > kMaxM)
         return PROJ_ERR_M;
     if (!cfg)
         return PROJ_ERR_NULL;
-    proj_config c = plan_default(layer, m);
+    proj_config c = plan_default(layer, m, g_layers[layer].zcr);
     Launch L;
-    int rc = resolve(layer, m, c, L);
+    int rc = resolve(layer, m, c, L, g_layers[layer]);
     if (rc)
         return rc;
     c.grid = L.grid;
@@ -780,7 +858,7 @@ int proj_out_cols(int layer, int m)
 {
     if (check_layer(layer))
         return PROJ_ERR_LAYER;
-    if (m < 1 || m > PROJ_MAX_M)
+    if (m < 1 || m > kMaxM)
         return PROJ_ERR_M;
     return n_eff_of(layer, m);
 }
@@ -897,6 +975,33 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
         *cfg = c;
     }
     return PROJ_OK;
+}
+
+int proj_split_giveups(int layer, int reset)
+{
+    if (check_layer(layer))
+        return PROJ_ERR_LAYER;
+    const LayerState &st = g_layers[layer];
+    if (!st.prepared)
+        return PROJ_ERR_NOT_PREPARED;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (dev != st.device)
+        return PROJ_ERR_DEVICE;
+    uint32_t n = 0;
+    if ((e = hipDeviceSynchronize()) != hipSuccess ||
+        (e = hipMemcpy(&n, st.giveups, sizeof n, hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_fail(e);
+    if (reset) {
+        // A partial published after its reducer gave up would read as
+        // arrived in a later launch: restore every mark, then the count.
+        if ((e = hipMemset(st.pws, 0xff, kWsBytes)) != hipSuccess ||
+            (e = hipMemset(st.giveups, 0, sizeof n)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess)
+            return hip_fail(e);
+    }
+    return (int)(n > 0x7fffffffu ? 0x7fffffffu : n);
 }
 
 int proj_compressed(int layer)

@@ -60,6 +60,9 @@ struct SkinnyArgs {
     int n_tt;                // token tiles (ceil(m / (16 * NT)))
     int ksplit;              // workgroups per tile along K
     int xcd_remap;           // 1: spread consecutive logical tiles on one XCD
+    uint32_t *giveups;       // split-K: incremented once per reducer wave that stops waiting
+    int poll_limit;          // split-K: polls of a word before the reducer stops waiting
+    int drop_publish;        // test only: splits that do not reduce exit without publishing
     // 12-bit weights (Z variants only)
     const uint32_t *wz;      // packed 12-bit fragments
     uint32_t wz_bytes;
@@ -422,12 +425,14 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     // it loads them all at once, re-reads the words still empty, marks every
     // word empty again, and sums through LDS in split order, taking its own
     // partial from registers at its place. The poll is bounded: after
-    // kPollLimit rounds the missing words count as NaN, so a launch always
-    // ends (and a lost partial shows in the output).
+    // a.poll_limit rounds the missing words count as NaN, so a launch always
+    // ends (and a lost partial shows in the output and in the give-up count).
     constexpr int EPT = (ELEMS + NTHR - 1) / NTHR;  // output elements per thread
     constexpr uint64_t kEmpty = ~0ull;              // two empty words
     uint64_t *wsw = a.pws + (size_t)tile * a.ksplit * ELEMS * 2;
     if (ks != rs) {
+        if (a.drop_publish)
+            return;
         for (int e = threadIdx.x; e < ELEMS; e += NTHR) {
             const u32x4 u = publishable(__builtin_bit_cast(u32x4, wave_sum(e)));
             uint64_t *d = wsw + ((size_t)ks * ELEMS + e) * 2;
@@ -454,7 +459,7 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
             // that waiting reducers add little traffic to the streams of the
             // splits still running; then read all and re-read stragglers.
             int poll = 0;
-            while (__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kEmpty && poll < kPollLimit)
+            while (__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kEmpty && poll < a.poll_limit)
                 ++poll;
             uint64_t wd[TILES][2];
 #pragma unroll
@@ -472,12 +477,16 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
                         miss |= wd[j][h] == kEmpty;
                 if (!__any(miss))
                     break;
-                if (poll >= kPollLimit) {
+                if (poll >= a.poll_limit) {
 #pragma unroll
                     for (int j = 0; j < TILES; ++j)
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
                             wd[j][h] = wd[j][h] == kEmpty ? 0x7fc000007fc00000ull : wd[j][h];
+                    // Visible to the host (proj_split_giveups); the marks of
+                    // this split are restored below like those of a complete one.
+                    if (lane == 0)
+                        __hip_atomic_fetch_add(a.giveups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
 #pragma unroll

@@ -50,7 +50,7 @@ enum proj_layer {
 enum proj_status {
     PROJ_OK = 0,
     PROJ_ERR_LAYER = -1,        /* layer id not in 0..4 */
-    PROJ_ERR_M = -2,            /* m < 1, or m above PROJ_MAX_M */
+    PROJ_ERR_M = -2,            /* m < 1 or m > 2^30 */
     PROJ_ERR_NULL = -3,         /* a required pointer is NULL */
     PROJ_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
     PROJ_ERR_NOT_PREPARED = -5, /* proj_run before proj_prepare for that layer */
@@ -58,9 +58,6 @@ enum proj_status {
     PROJ_ERR_HIP = -7,          /* a HIP runtime call failed (see proj_last_hip_error) */
     PROJ_ERR_DEVICE = -8        /* current device differs from the one the layer was prepared on */
 };
-
-/* Largest token count a call accepts (sizes the split-K workspace). */
-#define PROJ_MAX_M 4096
 
 /*
  * proj_prepare - repack a layer's weights once (guide ch. 1 §1.6: prepare runs
@@ -76,10 +73,20 @@ enum proj_status {
  *    the null stream and synchronizes the device. For the router (all 256
  *    rows) and the unpooler (its first 1024 rows) it also keeps a plain
  *    row-major copy of those rows for the row-dot kernel used at m <= 8
- *    (8 MB each). Preparing a prepared layer
- *    replaces its weights. The device current at this call becomes the
- *    layer's device.
- * Errors: PROJ_ERR_LAYER, PROJ_ERR_NULL, PROJ_ERR_ALIGN, PROJ_ERR_HIP.
+ *    (8 MB each). Then it warms up (guide ch. 10 "Measure, experiment, and
+ *    try your own changes", Experiment D): every token count up to 16384 is
+ *    planned and resolved (past that the plans reuse the same kernels), and
+ *    each distinct kernel the plans name is launched once on zero
+ *    activations, so no proj_run meets an unsupported configuration or pays
+ *    a first launch. The device current at this call becomes the layer's
+ *    device.
+ *    Preparing a prepared layer replaces its weights: the new state is built
+ *    and warmed up next to the old one, which is freed only on success (on
+ *    an error the layer keeps its previous weights). Replacing or releasing a
+ *    layer frees the buffers that graphs captured earlier point to: such
+ *    graphs must not be replayed afterwards.
+ * Errors: PROJ_ERR_LAYER, PROJ_ERR_NULL, PROJ_ERR_ALIGN, PROJ_ERR_HIP;
+ *    PROJ_ERR_UNSUPPORTED if a plan names a kernel that is not built.
  */
 int proj_prepare(int layer, const void *W);
 
@@ -91,9 +98,13 @@ int proj_prepare(int layer, const void *W);
  * out: device, m x proj_out_cols(layer, m) row-major, BF16 bits (router:
  *      FP32), 16-byte aligned. Fully overwritten.
  * stream: hipStream_t (NULL = null stream).
+ * m:   any token count from 1 to 2^30 (offsets are computed in 64 bits;
+ *      x and out must hold m rows; above 2^30 x alone would exceed 2 TB).
  * Effect: exactly one kernel launch on `stream`. No allocation, no
  *    synchronization, no host read of device memory, no memset; the choice
- *    of kernel depends on (layer, m) only. Safe to capture in a HIP graph and
+ *    of kernel depends on (layer, m) and on whether prepare built the
+ *    layer's 12-bit form (proj_compressed(layer) >= 0, fixed per prepared
+ *    weights), never on data. Safe to capture in a HIP graph and
  *    replay with new contents of x. Split-K state (arrival counters, or the
  *    empty marks of the polled partials) is restored on the GPU by the
  *    kernel itself.
@@ -128,6 +139,20 @@ int proj_layer_dims(int layer, int *N, int *K, int *w_elem_bytes, int *out_elem_
  * PROJ_ERR_NOT_PREPARED otherwise. Host-only; no GPU call.
  */
 int proj_compressed(int layer);
+
+/*
+ * proj_split_giveups - how many times a polled split-K reducer of this layer
+ * (kind 0 with ksplit > 1) stopped waiting for a partial since prepare or the
+ * last reset. Each give-up wrote NaN where the missing partial belonged (the
+ * bounded wait of the kind-0 configuration notes below). A partial published
+ * after its reducer gave up would leave words that a later launch reads as
+ * arrived, so reset != 0 also restores every empty mark of the layer's
+ * workspace before zeroing the count. Synchronizes the device; not for use
+ * inside a graph capture or while a proj_run of the layer is in flight on
+ * another stream. Returns the count (>= 0) or PROJ_ERR_LAYER,
+ * PROJ_ERR_NOT_PREPARED, PROJ_ERR_DEVICE, PROJ_ERR_HIP.
+ */
+int proj_split_giveups(int layer, int reset);
 
 /* proj_release - free a layer's packed weights and workspace; idempotent. */
 int proj_release(int layer);
@@ -165,7 +190,8 @@ int proj_last_hip_error(void);
  *             kinds 1 and 3 the last to arrive, counted with an atomic;
  *             kind 0 the one the hardware dispatches last, which polls the
  *             others' partials (a bounded wait: after 2^18 polls missing
- *             words read as NaN, so a launch always ends))
+ *             words read as NaN, so a launch always ends, and the give-up
+ *             is counted for proj_split_giveups))
  *   flags     bit 0 set: workgroup i keeps tile i. Clear (default): when the
  *             grid is a multiple of 8, consecutive tiles are grouped on one
  *             XCD (workgroups are dealt to the 8 XCDs round-robin).
@@ -178,6 +204,10 @@ int proj_last_hip_error(void);
  *             equal contiguous shares, a share may finish one tile and start
  *             the next, and the workgroups sharing a tile sum their parts in
  *             workgroup order (the last to arrive stores the tile).
+ *             bit 4 set (kind 0, tests only): the splits that do not reduce
+ *             exit without publishing and the reducer polls once, so every
+ *             reducer gives up (NaN outputs, counted by proj_split_giveups);
+ *             a host-forced stand-in for a split that never arrives.
  *             Other bits, or a bit the kind does not use, are rejected.
  * proj_plan fills the configuration proj_run would use; proj_run_config runs
  * an explicit one and returns PROJ_ERR_UNSUPPORTED if it is not compiled or

@@ -27,10 +27,12 @@ extern "C" {
  * proj_bench_flush - read `bytes` of device memory at `buf` (16-byte aligned,
  * bytes a multiple of 16). `sink` (device, at least 4096 uint32) receives a
  * word only when a data-dependent test on the values read succeeds, which
- * keeps every read live without a reduction. Used with a buffer of 1 GiB or
- * more to evict L2 and the Infinity Cache.
+ * keeps every read live without a reduction. mode 0: non-temporal loads;
+ * mode 1: plain loads (allocate in every cache level like the GEMV kernels'
+ * weight stream). Used with a buffer of 1 GiB or more to evict L2 and the
+ * Infinity Cache; other modes return PROJ_ERR_UNSUPPORTED.
  */
-int proj_bench_flush(const void *buf, size_t bytes, void *sink, void *stream);
+int proj_bench_flush(const void *buf, size_t bytes, void *sink, int mode, void *stream);
 
 /*
  * proj_bench_read_floor - pure streaming read of `bytes` at `buf` (16-byte
@@ -38,12 +40,28 @@ int proj_bench_flush(const void *buf, size_t bytes, void *sink, void *stream);
  * stream: 16 bytes per lane, each wave reading its own contiguous run 1 KB
  * per load, `unroll` loads in flight per lane (1, 2, 4 or 8). `grid`
  * workgroups (0 = 1024) of `waves` wavefronts (0 = 8, at most 16) each read
- * a contiguous share. `sink` (device, at least `grid` uint32 words) is
- * written as for proj_bench_flush. ev_start/ev_stop: NULL, or events from
- * proj_bench_event_create that then bracket exactly this kernel's execution.
+ * a contiguous share; mode 0 non-temporal loads, mode 1 plain loads. `sink`
+ * (device, at least `grid` uint32 words) is written as for proj_bench_flush.
+ * ev_start/ev_stop: NULL, or events from proj_bench_event_create that then
+ * bracket exactly this kernel's execution.
  */
 int proj_bench_read_floor(const void *buf, size_t bytes, void *sink, void *stream,
-                          int grid, int waves, int unroll, void *ev_start, void *ev_stop);
+                          int grid, int waves, int unroll, int mode, void *ev_start, void *ev_stop);
+
+/*
+ * proj_bench_stamp - one single-wave kernel that writes the GPU's
+ * constant-rate wall clock (64-bit, ticking at proj_bench_wallclock_khz) to
+ * ((uint64_t *)buf)[idx] (buf device, 8-byte aligned). Captured into a
+ * graph before and after a load's kernels, two stamps give the span of
+ * those kernels on the GPU (the gaps between them included), a replay's
+ * time without the host launch path (guide ch. 1 §1.4 times graph
+ * replays; the report's round 3 found the gaps between kernels worth a
+ * microsecond each).
+ */
+int proj_bench_stamp(void *buf, int idx, void *stream);
+
+/* proj_bench_wallclock_khz - tick rate of the proj_bench_stamp clock, in kHz. */
+int proj_bench_wallclock_khz(int *khz);
 
 /*
  * proj_run_timed - proj_run (cfg == NULL) or proj_run_config (cfg != NULL)

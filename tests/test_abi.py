@@ -56,7 +56,11 @@ def test_host_side_errors_without_gpu(lib):
     assert lib.proj_out_cols(5, 1) == -1
     assert lib.proj_out_cols(-1, 1) == -1
     assert lib.proj_out_cols(0, 0) == -2
-    assert lib.proj_out_cols(0, binding.PROJ_MAX_M + 1) == -2
+    assert lib.proj_out_cols(0, (1 << 30) + 1) == -2
+    assert lib.proj_out_cols(0, 1 << 30) == 2304         # any m from 1 to 2^30
+    assert lib.proj_out_cols(3, 4097) == 8192
+    assert lib.proj_split_giveups(9, 0) == -1
+    assert lib.proj_split_giveups(4, 0) == -5             # not prepared here
     assert lib.proj_run(7, vp(16), 1, vp(16), vp(0)) == -1
     assert lib.proj_run(0, vp(16), 0, vp(16), vp(0)) == -2
     assert lib.proj_run(0, vp(0), 1, vp(16), vp(0)) == -3
@@ -75,7 +79,8 @@ def test_dispatch_plans_tile_every_layer(lib):
     # Every (layer, m) resolves to a compiled variant that tiles the layer exactly.
     for name in layers.LAYERS:
         n, k, _, _ = layers.DIMS[name]
-        for m in list(range(1, 41)) + [64, 100, 127, 128, 129, 130, 200, 256, 512, 1000, 4096]:
+        for m in list(range(1, 41)) + [64, 100, 127, 128, 129, 130, 200, 256, 512, 1000, 4096, 4097, 8192, 8193,
+                                       100000, 1 << 24, 1 << 30]:
             cfg = binding.proj_plan(name, m)
             ne = layers.n_eff(name, m)
             assert cfg.block == 64 * (cfg.waves + (1 if cfg.flags & 4 else 0))
@@ -136,3 +141,41 @@ def test_large_m_split_counts_keep_one_workgroup_per_cu(lib):
                 assert cfg.grid <= 256, (name, m, cfg.as_dict())
                 tiles = cfg.grid // cfg.ksplit
                 assert tiles * (cfg.ksplit + 1) > 256 or cfg.ksplit == 4, (name, m, cfg.as_dict())
+
+
+def test_router_past_8192_tokens_drops_the_split(lib):
+    # The polled split's partials grow with m; past 8192 tokens they would not
+    # fit the 32 MB workspace, so the plan keeps the whole K range in one
+    # workgroup (16 waves x 16 k-steps).
+    for m in (256, 4096, 8192):
+        assert binding.proj_plan("router", m).ksplit == 4, m
+    for m in (8193, 20000, 1 << 20):
+        cfg = binding.proj_plan("router", m)
+        assert (cfg.kind, cfg.waves, cfg.spw, cfg.ksplit) == (0, 16, 16, 1), (m, cfg.as_dict())
+
+
+def test_binding_rejects_bad_tensors_before_launch():
+    # Shapes, dtypes, layout and placement are checked on the host; nothing
+    # reaches the library (which is not even consulted for these).
+    import torch
+
+    bf, f32 = torch.bfloat16, torch.float32
+    good_x = torch.zeros((4, 1024), dtype=bf)
+    good_out = torch.zeros((4, 8192), dtype=bf)
+    cases = [
+        ("o", torch.zeros((4, 1000), dtype=bf), good_out, "shape"),          # wrong K
+        ("o", torch.zeros((3, 1024), dtype=bf), good_out, "shape"),          # fewer than m rows
+        ("o", torch.zeros((4, 1024), dtype=f32), good_out, "dtype"),         # x not BF16
+        ("o", good_x, torch.zeros((4, 4096), dtype=bf), "shape"),            # wrong out width
+        ("o", good_x, torch.zeros((4, 8192), dtype=f32), "dtype"),           # BF16 layer, FP32 out
+        ("o", torch.zeros((1024, 4), dtype=bf).t(), good_out, "contiguous"), # transposed view
+        ("o", torch.zeros((4, 2048), dtype=bf)[:, ::2], good_out, "contiguous"),
+        ("router", torch.zeros((4, 8192), dtype=bf), torch.zeros((4, 256), dtype=bf), "dtype"),
+        ("unpooler", torch.zeros((4, 4096), dtype=bf), torch.zeros((4, 8192), dtype=bf), "shape"),  # slice: 1024
+        ("o", good_x, good_out, "not a GPU"),                                # right shapes, CPU memory
+    ]
+    for layer, x, out, what in cases:
+        with pytest.raises(ValueError, match=what):
+            binding.proj_run(layer, x, 4, out)
+        with pytest.raises(ValueError, match=what):
+            binding.proj_run_config(layer, x, 4, out, binding.ProjConfig.make())

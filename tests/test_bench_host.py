@@ -18,9 +18,10 @@ def test_kernel_names_match_the_templates():
     assert bench.kernel_name(_cfg(0, 1, 1, 8, 32), False) == "skinny_kernel<1, 1, 8, 32, false, false>"
     assert bench.kernel_name(_cfg(0, 1, 1, 8, 32, flags=4), False) == "skinny_kernel<1, 1, 8, 32, false, true>"
     assert bench.kernel_name(_cfg(0, 2, 1, 4, 16, 4), True) == "skinny_kernel<2, 1, 4, 16, true, false>"
-    assert bench.kernel_name(_cfg(3, 4, 8, 4, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false>"
-    assert bench.kernel_name(_cfg(3, 4, 8, 4, 16, 2), False) == "wide_kernel<2, 4, 16, 4, false, false>"
-    assert bench.kernel_name(_cfg(3, 2, 4, 4, 8, 256, 8), True) == "wide_kernel<1, 2, 8, 2, true, true>"
+    assert bench.kernel_name(_cfg(3, 4, 8, 4, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false, 4>"
+    assert bench.kernel_name(_cfg(3, 4, 8, 4, 16, 2), False) == "wide_kernel<2, 4, 16, 4, false, false, 4>"
+    assert bench.kernel_name(_cfg(3, 2, 4, 4, 8, 256, 8), True) == "wide_kernel<1, 2, 8, 2, true, true, 4>"
+    assert bench.kernel_name(_cfg(3, 4, 16, 8, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false, 8>"
     assert bench.kernel_name(_cfg(1, 2, 8, 4, 8), False) == "tiled_kernel<2, 2, 4, 4, 8, false>"
     assert bench.kernel_name(_cfg(2, 8, 1, 4, 4), True) == "rowdot_kernel<8, 1, 4, true>"
 
@@ -93,35 +94,83 @@ def test_pmc_summary_refuses_a_pass_with_missing_launches(tmp_path):
         bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
 
 
+TRACE_FIELDS = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"]
+
+
 def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
-    steps, warmup, load_reps, graph_reps, awkward_reps = 3, 1, 2, 2, 1
-    seq = bench.call_sequence(steps, warmup, load_reps, graph_reps, awkward_reps)
+    counts = (3, 1, 2, 1, 2)     # steps, warmup, study reps, awkward reps, graph reps
+    seq = bench.call_sequence(*counts)
     path = tmp_path / "trace.csv"
     with open(path, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"])
+        w = csv.DictWriter(f, fieldnames=TRACE_FIELDS)
         w.writeheader()
         t = 0
-        for i, (name, layer) in enumerate(seq):
-            w.writerow({"Kernel_Name": "gdp::(anonymous namespace)::flush_kernel(x)", "Start_Timestamp": t,
+        for i, (tag, layer, m) in enumerate(seq):
+            w.writerow({"Kernel_Name": "gdp::(anonymous namespace)::flush_kernel<false>(x)", "Start_Timestamp": t,
                         "End_Timestamp": t + 100000, "Grid_Size_X": 1})
             t += 100000
-            dur = 1000 * (LAYERS.index(layer) + 1) + LOADS.get(name, 999)   # ns
-            w.writerow({"Kernel_Name": "void gdp::wide_kernel<2, 4, 8, 2, false, false>(a)", "Start_Timestamp": t,
-                        "End_Timestamp": t + dur, "Grid_Size_X": 256})
+            dur = 1000 * (LAYERS.index(layer) + 1) + m + (500 if tag == "warmup" else 0)   # ns
+            w.writerow({"Kernel_Name": "void gdp::wide_kernel<2, 4, 8, 2, false, false, 4>(a)",
+                        "Start_Timestamp": t, "End_Timestamp": t + dur, "Grid_Size_X": 256})
             t += dur
-    r = bench.summarize_loads_trace(str(path), steps, warmup, load_reps, graph_reps, awkward_reps)
+    r = bench.summarize_loads_trace(str(path), *counts)
+    assert "warmup" not in r
     for name, m in LOADS.items():
         lay = r[name]["layers"]
+        assert r[name]["m"] == m
         for layer in LAYERS:
+            assert lay[layer]["n"] == counts[0]
             assert lay[layer]["median_us"] == pytest.approx((1000 * (LAYERS.index(layer) + 1) + m) / 1e3)
-            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false>"
+            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false, 4>"
+        assert r["graph:" + name]["layers"]["o"]["n"] == counts[4]
     for m in AWKWARD_M:
         assert r["m=%d" % m]["m"] == m
-        for layer in LAYERS:
-            assert r["m=%d" % m]["layers"][layer]["median_us"] == pytest.approx((1000 * (LAYERS.index(layer) + 1) + 999) / 1e3)
-            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false>"
+    assert r["study:none"]["layers"]["pooler"]["n"] == counts[2]
     with pytest.raises(SystemExit):
-        bench.summarize_loads_trace(str(path), steps + 1, warmup, load_reps, graph_reps, awkward_reps)
+        bench.summarize_loads_trace(str(path), counts[0] + 1, *counts[1:])
+
+
+def _graph_trace(path, reps, gap_ns=700):
+    """A kernel trace of the graph leg: per load, `reps` pairs of (load graph,
+    floor graph), each a stamp, five kernels, a stamp, separated by flushes."""
+    t = 0
+    rows = []
+
+    def add(name, dur):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur, "Grid_Size_X": 1})
+        t += dur + gap_ns
+    for j, name in enumerate(bench.LOAD_ORDER):
+        for r in range(reps):
+            for which in (("load", "floor") if r % 2 == 0 else ("floor", "load")):
+                add("gdp::(anonymous namespace)::flush_kernel<false>(a)", 200000)
+                add("gdp::(anonymous namespace)::stamp_kernel(a, b)", 1000)
+                for i, layer in enumerate(LAYERS):
+                    k = ("void gdp::skinny_kernel<1, 1, 8, 32, false, false>(a)" if which == "load"
+                         else "gdp::(anonymous namespace)::read_floor_kernel<4, false>(a)")
+                    add(k, 1000 * (i + 1) + (100 * j if which == "load" else 0))
+                add("gdp::(anonymous namespace)::stamp_kernel(a, b)", 1000)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=TRACE_FIELDS)
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_graph_trace_summary_gives_kernels_gaps_and_span(tmp_path):
+    _graph_trace(tmp_path / "g.csv", 3)
+    r = bench.summarize_graph_trace(str(tmp_path / "g.csv"), 3)
+    assert list(r) == list(bench.LOAD_ORDER)
+    for j, name in enumerate(bench.LOAD_ORDER):
+        g, fl = r[name]["graph"], r[name]["floor_graph"]
+        assert g["kernel_median_us"] == pytest.approx([(1000 * (i + 1) + 100 * j) / 1e3 for i in range(5)])
+        assert fl["kernel_median_us"] == pytest.approx([i + 1.0 for i in range(5)])
+        assert g["gap_median_us"] == pytest.approx([0.7] * 6)
+        assert g["span_median_us"] == pytest.approx(sum(g["kernel_median_us"]) + 4 * 0.7)
+        assert g["kernels"][0].startswith("skinny_kernel") and g["n"] == 3
+    page = bench.md_graph_trace(r, "g.csv", 3)
+    assert "median gap is 0.70 us" in page
+    with pytest.raises(SystemExit):
+        bench.summarize_graph_trace(str(tmp_path / "g.csv"), 4)
 
 
 def test_profile_pages_render(tmp_path):
@@ -131,7 +180,16 @@ def test_profile_pages_render(tmp_path):
     pm = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
     page = bench.md_pmc(pm, ["f.csv", "w.csv"], ["f.log", "w.log"])
     assert page.count("\n| ") >= len(LOADS) * len(LAYERS) and "rocprofv3 --pmc FETCH_SIZE" in page
-    tr = {l: {"kernel": "skinny_kernel<1, 1, 8, 32, false, false>", "grid": 64, "n": 3, "mean_us": 5.0,
-              "median_us": 5.0} for l in LAYERS}
-    page = bench.md_decode1_trace(tr, "t.csv")
-    assert "Sum of the five trace medians: 25.00 us" in page and "--kernel-trace" in page
+    line = {"flush_study": {"reps": 5, "chosen": "plain-1GiB",
+                            "conditions": {c: {"floor_us": 11.0 + i, "pooler_decode1_us": 9.0 + i}
+                                           for i, (c, _, _) in enumerate(bench.STUDY_CONDITIONS)}}}
+    page = bench.md_flush_study(line, "b.json")
+    assert "| plain-2GiB | 14.00 | 12.00 |" in page and "`plain-1GiB` flush" in page
+
+
+def test_stored_bytes_of_12bit_kernels():
+    cfg = _cfg(0, 1, 1, 8, 32, flags=4)
+    w = rf.weight_bytes("pooler", 1)
+    assert bench.stored_bytes("pooler", 1, cfg, 7) == rf.bytes_of("pooler", 1) - w // 4 + 4096 * 7 * 8
+    assert bench.stored_bytes("pooler", 1, _cfg(0, 1, 1, 8, 32), 7) == rf.bytes_of("pooler", 1)
+    assert bench.mfma_flops("router", 256) == 3 * rf.flops_of("router", 256)

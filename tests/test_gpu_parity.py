@@ -67,11 +67,12 @@ def test_o_projection_m1(variant):
 @pytest.mark.parametrize("outliers", [False, True], ids=["normal", "outlier"])
 @pytest.mark.parametrize("layer", LAYERS)
 @pytest.mark.parametrize("load", list(LOADS))
-def test_loads(load, layer, outliers):
-    p = prepared(0)
+@pytest.mark.parametrize("wseed", [0, 1])
+def test_loads(wseed, load, layer, outliers):
+    p = prepared(wseed)
     m = LOADS[load]
-    xs = make_x(layer, m, seed=200, outliers=outliers)
-    say("load", load, layer, "m=%d" % m, "outliers" if outliers else "normal")
+    xs = make_x(layer, m, seed=200 + wseed, outliers=outliers)
+    say("load", load, layer, "m=%d" % m, "wseed=%d" % wseed, "outliers" if outliers else "normal")
     got = run_layer(layer, xs.bits)
     r = compare(layer, got, p.w[layer], xs)
     assert r.ok, r
@@ -92,15 +93,16 @@ def test_awkward_m(wseed, m, layer, outliers):
 
 
 @pytest.mark.parametrize("layer", LAYERS)
-def test_max_token_count(layer):
-    """The largest m the library accepts (PROJ_MAX_M), checked on sampled rows
-    (every probe row, the first and last rows and random ones)."""
+@pytest.mark.parametrize("m", [4096, 4097, 8192])
+def test_large_token_counts(m, layer):
+    """Any m >= 1 is a valid call; large ones (the router's split partials
+    stop fitting its workspace past 8192 tokens) are checked on sampled rows
+    (every probe row, the first and last rows and random ones), all outputs
+    finite."""
     p = prepared(0)
-    m = binding.PROJ_MAX_M
     xs = make_x(layer, m, seed=1100, outliers=True)
-    say("max m", layer, "m=%d" % m)
+    say("large m", layer, "m=%d" % m, binding.proj_plan(layer, m).as_dict())
     got = run_layer(layer, xs.bits)
-    assert np.all(np.isfinite(got))
     r = compare(layer, got, p.w[layer], xs, sample_rows(xs, m))
     assert r.ok, r
 
@@ -340,6 +342,66 @@ def test_graph_replay_fresh_inputs(layer, m):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32),
                        prev_bits.view(torch.int16) if out.dtype == torch.bfloat16 else prev_bits.view(torch.int32))
+
+
+@pytest.mark.parametrize("layer,m", [("router", 16), ("qkv_gate", 32), ("pooler", 256), ("unpooler", 1)])
+def test_first_call_after_prepare_captured_in_graph(layer, m):
+    """Prepare warms every kernel its plans can pick, so the very first
+    proj_run of a freshly prepared layer may be the one captured in a graph;
+    the replays are exact and bit identical."""
+    _dirty()
+    w = make_weight(layer, 3)
+    binding.proj_prepare(layer, to_device_weight(layer, w))
+    torch.cuda.synchronize()
+    k = SHAPES[layer][1]
+    x_static = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
+    out = binding.new_out(layer, m)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.proj_run(layer, x_static, m, out, s)   # first call of the layer since prepare
+    say("first call captured", layer, "m=%d" % m)
+    first = None
+    for rep in range(3):
+        xs = make_x(layer, m, seed=1500 + rep % 2, outliers=True)
+        x_static.copy_(to_device_x(xs.bits))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_to_f64(out)
+        r = compare(layer, got, w, xs, sample_rows(xs, m) if m >= 100 else None)
+        assert r.ok, (rep, r)
+        if rep == 0:
+            first = got
+        if rep == 2:
+            assert np.array_equal(got, first)
+    _dirty()
+
+
+@pytest.mark.parametrize("layer,m", [("router", 32), ("qkv_gate", 32)])
+def test_split_giveup_is_counted_and_cleaned(layer, m):
+    """A polled split-K reducer that stops waiting is visible to the host. The
+    test configuration (flags bit 4) makes the splits that do not reduce drop
+    their partials and the reducer poll once: every kernel still exits at
+    once, the missing partials read NaN, each give-up is counted, the marks
+    are restored, and the next launch of the normal plan is exact."""
+    p = prepared(0)
+    assert binding.proj_split_giveups(layer, reset=True) == 0
+    ks = SHAPES[layer][1] // 32
+    cfg = binding.ProjConfig.make(kind=0, nt=2, rb=1, waves=8, spw=ks // 32, ksplit=4, flags=16)
+    xs = make_x(layer, m, seed=1600, outliers=True)
+    say("forced give-up", layer, "m=%d" % m, cfg.as_dict())
+    got = run_layer(layer, xs.bits, cfg=cfg)
+    assert np.isnan(got).all()
+    n_tiles = (SHAPES[layer][0] // 16) * -(-m // 32)
+    assert binding.proj_split_giveups(layer) == n_tiles * 3        # one per reducer wave and missing split
+    for c in (binding.proj_plan(layer, m), binding.ProjConfig.make(kind=0, nt=2, rb=1, waves=8, spw=ks // 32,
+                                                                    ksplit=4)):
+        got = run_layer(layer, xs.bits, cfg=c)
+        r = compare(layer, got, p.w[layer], xs)
+        assert r.ok, (c.as_dict(), r)
+    assert binding.proj_split_giveups(layer, reset=True) == n_tiles * 3
+    assert binding.proj_split_giveups(layer) == 0
 
 
 def _exception_columns(w, limit=3):
