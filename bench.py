@@ -2,24 +2,38 @@
 """Cold-cache benchmark of the five decode projections on one MI355X.
 
 Metric: cold-cache microseconds per load (the sum of its five layers' times)
-plus achieved HBM bandwidth against the roofline. Loads, layers and the
-cold-cache protocol follow guide ch. 1 "The problem, the judge and the speed
-of light" (§1.2 loads, §1.3 a load's time is the sum of its five shapes, §1.4
-a buffer larger than the cache is read before every timed call).
+plus achieved HBM bandwidth against the roofline, over the six loads m = 1 to
+256. Loads, layers and the cold-cache rule follow guide ch. 1 "The problem,
+the judge and the speed of light" (§1.2 the loads, §1.3 a load's time is the
+sum of its five shapes, §1.4 a buffer larger than the cache is read before
+every timed call, and calls are replayed from a graph).
 
-Protocol per timed call: a 1 GiB read-only flush kernel (more than the 32 MB
-of L2 plus the 256 MB Infinity Cache), then the projection kernel launched
-with a pair of HIP events that the runtime stamps at the start and end of
-that kernel's execution (hipExtLaunchKernel), then a sync. The flush is
-outside the measured interval.
+One step runs every load once: 6 loads x 5 layers = 30 cold calls. Each call
+is a flush (a read of FLUSH_BYTES, more than the 32 MB of L2 plus the 256 MB
+Infinity Cache; the flush study below picks its kind) followed by the
+projection kernel, launched with a pair of HIP events that the runtime stamps
+at the start and end of that kernel's own execution (hipExtLaunchKernel), on
+the stream the kernel runs on. The headline `value` is the median over the
+timed steps of the step's sum of 30 kernel durations, i.e. the sum of the six
+per-load times. Inputs are seeded synthetic tensors resident in device memory
+before timing starts; weights are prepared (repacked) before timing.
 
-A step is one decode-1 load (m = 1, all five layers, cold before each layer):
-the headline `value` is the median over the timed steps of the per-step sum.
-The other loads (decode-16/32, verify-1/16/32) are measured the same way and
-reported under `loads` (with achieved TB/s and TFLOP/s). `graph_replay`
-repeats every load with the pages' method (each call captured in a HIP graph,
-replayed cold, minus an empty-kernel graph) for context. Inputs are seeded synthetic tensors already resident
-in device memory; weights are prepared (repacked) before timing.
+Also reported, each from the same process:
+* per load and layer: median kernel time, achieved TB/s of the bytes the
+  kernel reads, the BF16-equivalent rate, and the fraction of a measured
+  cold read floor over the same bytes (the hand-written read kernel, best
+  of plain and non-temporal loads over several grid shapes, the GEMV's own
+  among them);
+* graph replay (the pages' method, guide ch. 10 "Measure, experiment, and
+  try your own changes" §10.1): each load captured as ONE graph of its five
+  kernels between two GPU wall-clock stamps, replayed cold, paired and
+  alternated with a graph of five read-floor kernels over the same bytes;
+  reported raw (host events around the replay) and as the stamped span;
+* the flush study: the 67 MB read floor and the pooler decode-1 kernel
+  with no flush, a 1 GiB non-temporal flush, a 1 GiB plain flush and a
+  2 GiB plain flush;
+* the awkward token counts (guide ch. 1 §1.2), timed like the loads;
+* the roofline of the dominant kernel and the CPU oracle's own times.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --pmc-pass     (short run used under rocprofv3 --pmc)
@@ -37,13 +51,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FLUSH_BYTES = 1 << 30
+GIB = 1 << 30
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
-# Pages' H200 per-load time for decode 1, best reported (guide ch. 1 §1.8 table).
-H200_DECODE1_US = 38.25
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_loads.json")
 LOAD_ORDER = ("decode-1", "decode-16", "decode-32", "verify-1", "verify-16", "verify-32")
+# Pages' H200 per-load times, best reported (guide ch. 1 §1.8 table): context
+# from other hardware, not a target.
+H200_BEST_US = {"decode-1": 38.25, "decode-16": 54.03, "decode-32": 63.77, "verify-1": 39.98,
+                "verify-16": 77.91, "verify-32": 94.80}
+
+# The flush used before every timed call: (mode, bytes). Chosen from the flush
+# study (the kind after which the kernels read coldest); 0 = non-temporal,
+# 1 = plain loads.
+FLUSH_MODE = 1
+FLUSH_BYTES = GIB
+FLUSH_BUF_BYTES = 2 * GIB
+STUDY_CONDITIONS = (("none", None, 0), ("nt-1GiB", 0, GIB), ("plain-1GiB", 1, GIB), ("plain-2GiB", 1, 2 * GIB))
+
+# Read-floor configurations tried for every byte count (grid, waves, unroll);
+# each in both load modes, plus the projection kernel's own grid and waves.
+FLOOR_CONFIGS = ((256, 8, 4), (256, 16, 2), (512, 8, 4), (1024, 8, 4), (2048, 4, 4), (4096, 4, 2))
 
 
 def log(*a):
@@ -74,6 +102,29 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+def stored_bytes(layer, m, cfg, zcr):
+    """Bytes the chosen kernel must read and write for one call: the
+    algorithmic bytes, except that a kernel on the 12-bit weights reads 3/4 of
+    the BF16 weight bytes plus the correction table (N rows x zcr slots x 8
+    bytes)."""
+    from gemv_decode_projections_amd import roofline as rf
+    from gemv_decode_projections_amd.layers import DIMS
+
+    b = rf.bytes_of(layer, m)
+    if cfg.kind == 0 and cfg.flags & 4:
+        n = DIMS[layer][0]
+        b = b - rf.weight_bytes(layer, m) // 4 + n * zcr * 8
+    return b
+
+
+def mfma_flops(layer, m):
+    """Matrix-core FLOPs the kernels issue: 2 m N K, three times that for the
+    router (its FP32 weights enter as three exact BF16 parts)."""
+    from gemv_decode_projections_amd import roofline as rf
+
+    return rf.flops_of(layer, m) * (3 if layer == "router" else 1)
+
+
 class Bench:
     def __init__(self, seed=0):
         import numpy as np
@@ -93,12 +144,18 @@ class Bench:
                   else torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)).to(self.dev)
             B.proj_prepare(layer, wd)
             del wd
-        self.flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=self.dev)
+        self.flush_buf = torch.ones(FLUSH_BUF_BYTES, dtype=torch.uint8, device=self.dev)
         self.sink = torch.zeros(1 << 16, dtype=torch.int32, device=self.dev)
         self.floor_buf = torch.ones(80 << 20, dtype=torch.uint8, device=self.dev)
+        self.stamps = torch.zeros(64, dtype=torch.int64, device=self.dev)
         self.timer = B.KernelTimer()
         self.inputs = {}
+        self.floor_cfg = {}
         torch.cuda.synchronize()
+
+    def flush(self, mode=FLUSH_MODE, nbytes=FLUSH_BYTES, stream=None):
+        if mode is not None:
+            self.B.proj_bench_flush(self.flush_buf, self.sink, stream, mode=mode, nbytes=nbytes)
 
     def xin(self, layer, m, variant=0):
         key = (layer, m, variant)
@@ -108,89 +165,131 @@ class Bench:
             self.inputs[key] = (x, self.B.new_out(layer, m, device=self.dev))
         return self.inputs[key]
 
-    def kernel_us(self, layer, m, variant=0):
+    def kernel_us(self, layer, m, variant=0, flush=(FLUSH_MODE, FLUSH_BYTES)):
         """One cold call: flush, then the projection kernel timed by its own events."""
         x, out = self.xin(layer, m, variant)
-        self.B.proj_bench_flush(self.flush, self.sink)
+        self.flush(*flush)
         self.B.proj_run_timed(layer, x, m, out, self.timer)
         return self.timer.elapsed_us()
 
-    def graph_us(self, layer, m, reps):
-        """Median cold time of one captured proj_run replayed as a HIP graph.
+    def floor_once(self, nbytes, cfg, flush=(FLUSH_MODE, FLUSH_BYTES)):
+        grid, waves, unroll, mode = cfg
+        self.flush(*flush)
+        self.B.proj_bench_read_floor(self.floor_buf, nbytes, self.sink, grid, waves, unroll,
+                                     events=self.timer, mode=mode)
+        return self.timer.elapsed_us()
 
-        Events are recorded on the replay stream around graph.replay(), so the
-        time includes the graph launch overhead; graph_net_us subtracts the
-        same measurement of a graph holding one empty kernel.
-        """
-        torch, B = self.torch, self.B
-        x, out = self.xin(layer, m, 0) if layer is not None else (None, None)
+    def floor_us(self, nbytes, reps, extra=()):
+        """Cold pure-read time of `nbytes` (rounded up to 16): the best median
+        over the read kernel's configurations (both load modes); the best
+        configuration is kept for the graph leg."""
+        nbytes = (nbytes + 15) // 16 * 16
+        best = None
+        cfgs = [c + (mode,) for c in tuple(FLOOR_CONFIGS) + tuple(extra) for mode in (0, 1)]
+        for cfg in cfgs:
+            med = statistics.median(self.floor_once(nbytes, cfg) for _ in range(reps))
+            if best is None or med < best[0]:
+                best = (med, cfg)
+        self.floor_cfg[nbytes] = best[1]
+        return best[0], best[1]
+
+    # -------------------------------------------------------------- graphs
+
+    def capture(self, fn):
+        """A HIP graph of fn(stream), captured on a side stream."""
+        torch = self.torch
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            if layer is None:
-                B.proj_bench_empty(s)
-            else:
-                B.proj_run(layer, x, m, out, s)
-        torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            if layer is None:
-                B.proj_bench_empty(s)
-            else:
-                B.proj_run(layer, x, m, out, s)
+            fn(s)
+        torch.cuda.synchronize()
+        return g, s
+
+    def load_graph(self, name):
+        """Stamp 0, the load's five projection kernels back to back, stamp 1."""
+        m = self.LOADS[name]
+        xs = {l: self.xin(l, m, 0) for l in self.LAYERS}
+
+        def body(s):
+            self.B.proj_bench_stamp(self.stamps, 0, s)
+            for l in self.LAYERS:
+                x, out = xs[l]
+                self.B.proj_run(l, x, m, out, s)
+            self.B.proj_bench_stamp(self.stamps, 1, s)
+        return self.capture(body)
+
+    def floor_graph(self, byte_counts):
+        """Stamp 2, one read-floor kernel per layer over its bytes (best configuration), stamp 3."""
+        def body(s):
+            self.B.proj_bench_stamp(self.stamps, 2, s)
+            for nb in byte_counts:
+                nb = (nb + 15) // 16 * 16
+                grid, waves, unroll, mode = self.floor_cfg[nb]
+                self.B.proj_bench_read_floor(self.floor_buf, nb, self.sink, grid, waves, unroll, stream=s, mode=mode)
+            self.B.proj_bench_stamp(self.stamps, 3, s)
+        return self.capture(body)
+
+    def replay(self, g, s):
+        """Cold replay: flush on the replay stream, then the graph between two
+        host-recorded events. Returns (event us, stamped span us)."""
+        torch = self.torch
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ts = []
-        for _ in range(reps):
-            with torch.cuda.stream(s):
-                B.proj_bench_flush(self.flush, self.sink, s)
-                e0.record(s)
-                g.replay()
-                e1.record(s)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        return statistics.median(ts)
-
-    def floor_us(self, nbytes, reps):
-        """Cold pure-read kernel over the same byte count (16-byte multiple)."""
-        nbytes = (nbytes + 15) // 16 * 16
-        best = None
-        for grid, waves, unroll in ((2048, 4, 4), (1024, 8, 4), (4096, 4, 2), (2048, 8, 2)):
-            ts = []
-            for _ in range(reps):
-                self.B.proj_bench_flush(self.flush, self.sink)
-                self.B.proj_bench_read_floor(self.floor_buf, nbytes, self.sink, grid, waves, unroll,
-                                             events=self.timer)
-                ts.append(self.timer.elapsed_us())
-            med = statistics.median(ts)
-            if best is None or med < best:
-                best = med
-        return best
+        with torch.cuda.stream(s):
+            self.flush(stream=s)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3
 
 
-def cpu_baseline(seconds):
-    """The CPU oracle on the decode-1 load (all five layers, m = 1) on the host cores."""
-    import numpy as np
-
+def cpu_baseline(layers, loads, reps_small=3):
+    """The CPU oracle on every load (the same shapes, its own full outputs) on
+    the host's cores: the median of `reps_small` runs per layer for m <= 32,
+    one run above; decode-1 also on one thread."""
     import oracle
-    from workload import LAYERS, make_weight, make_x
+    from workload import make_weight, make_x
 
-    ws = {l: make_weight(l, 0) for l in LAYERS}
-    xs = {l: make_x(l, 1, seed=1000) for l in LAYERS}
-    times = []
-    t_end = time.perf_counter() + seconds
-    while time.perf_counter() < t_end or len(times) < 3:
-        t0 = time.perf_counter()
-        for l in LAYERS:
-            oracle.reference(l, xs[l].bits, ws[l])
-        times.append((time.perf_counter() - t0) * 1e6)
+    ws = {l: make_weight(l, 0) for l in layers}
+    per_load = {}
+    t_all = time.perf_counter()
+    for name in LOAD_ORDER:
+        m = loads[name]
+        lay = {}
+        for l in layers:
+            xs = make_x(l, m, seed=1000)
+            ts = []
+            for _ in range(reps_small if m <= 32 else 1):
+                t0 = time.perf_counter()
+                oracle.reference(l, xs.bits, ws[l])
+                ts.append((time.perf_counter() - t0) * 1e6)
+            lay[l] = round(statistics.median(ts), 1)
+        per_load[name] = {"m": m, "us": round(sum(lay.values()), 1), "layers_us": lay}
+    nt = oracle.threads()
+    one = []
+    try:
+        oracle.set_threads(1)
+        xs1 = {l: make_x(l, 1, seed=1000) for l in layers}
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for l in layers:
+                oracle.reference(l, xs1[l].bits, ws[l])
+            one.append((time.perf_counter() - t0) * 1e6)
+    finally:
+        oracle.set_threads(nt)
+    total = sum(v["us"] for v in per_load.values())
     return {
-        "value": round(statistics.median(times), 1),
-        "unit": "us per decode-1 load",
-        "cores": oracle.threads(),
+        "value": round(total, 1),
+        "unit": "us per six-load set (sum of the six loads' five layers)",
+        "cores": nt,
         "kind": "oracle",
-        "sample": "%d full decode-1 loads (5 layers, m=1, all %d outputs each) in %.1f s on %s"
-                  % (len(times), sum(oracle.out_cols(l, 1) for l in LAYERS), sum(times) / 1e6, _cpu_name()),
+        "sample": "the whole workload: each load's five layers at its m, every output, FP64 oracle; median of %d "
+                  "runs per layer for m <= 32, one run above; %.1f s on %s" % (
+                      reps_small, time.perf_counter() - t_all, _cpu_name()),
+        "loads": per_load,
+        "decode1_single_thread_us": round(statistics.median(one), 1),
     }
 
 
@@ -234,9 +333,10 @@ def kernel_name(cfg, f32w):
     if cfg.kind == 1:   # <rows per wave, token blocks, waves, k-steps per super-step, depth, fp32>
         return "tiled_kernel<%d, %d, %d, %d, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.waves,
                                                          min(4, cfg.spw // 2), cfg.spw, f)
-    if cfg.kind == 3:   # <rows per wave, token blocks, depth, k-steps per super-step, fp32, stream>
-        return "wide_kernel<%d, %d, %d, %d, %s, %s>" % (cfg.rb // 4, cfg.nt, cfg.spw, 4 if cfg.spw >= 16 else 2, f,
-                                                       "true" if cfg.flags & 8 else "false")
+    if cfg.kind == 3:   # <rows per wave, token blocks, depth, k-steps per super-step, fp32, stream, waves>
+        return "wide_kernel<%d, %d, %d, %d, %s, %s, %d>" % (cfg.rb // cfg.waves, cfg.nt, cfg.spw,
+                                                           4 if cfg.spw >= 16 else 2, f,
+                                                           "true" if cfg.flags & 8 else "false", cfg.waves)
     return "rowdot_kernel<%d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.spw, f)
 
 
@@ -247,6 +347,10 @@ def _is_proj_kernel(name):
     return any(k in name for k in PROJ_KERNELS)
 
 
+def _short(name):
+    return name.split("(")[0].replace("void gdp::", "").replace("gdp::(anonymous namespace)::", "")
+
+
 def _read_csv(path):
     import csv
 
@@ -254,83 +358,112 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_trace(trace_csv, steps, warmup):
-    """Per-layer kernel durations of the timed decode-1 steps, from a rocprofv3 kernel trace of bench.py."""
-    from workload import LAYERS
+# ------------------------------------------------------- launch sequence
 
-    rows = sorted(_read_csv(trace_csv), key=lambda r: int(r["Start_Timestamp"]))
-    sk = [r for r in rows if _is_proj_kernel(r["Kernel_Name"])]
-    timed = sk[warmup * len(LAYERS):(warmup + steps) * len(LAYERS)]
-    out = {}
-    for i, layer in enumerate(LAYERS):
-        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed[i::len(LAYERS)]]
-        out[layer] = {"kernel": timed[i]["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
-                      "grid": int(timed[i]["Grid_Size_X"]), "n": len(d),
-                      "mean_us": round(statistics.mean(d), 3), "median_us": round(statistics.median(d), 3)}
-    return out
+def call_sequence(steps, warmup, study_reps, awkward_reps, graph_reps):
+    """(tag, layer, m) of every projection kernel bench.py launches, in launch
+    order: the event-timed steps (tag = load name, warm-up steps tagged
+    'warmup'), the flush study's pooler calls ('study:<condition>'), the
+    awkward token counts ('m=<m>') and the graph replays ('graph:<load>')."""
+    from workload import AWKWARD_M, LAYERS, LOADS
 
-
-def call_sequence(steps, warmup, load_reps, graph_reps, awkward_reps, graph=True):
-    """(load, layer) of every projection kernel bench.py launches, in launch order
-    (the awkward token counts appear as loads named "m=<m>")."""
-    from workload import AWKWARD_M, LAYERS
-
-    seq = [("decode-1", l) for _ in range(warmup + steps) for l in LAYERS]
-    for name in LOAD_ORDER[1:]:
-        for l in LAYERS:
-            seq += [(name, l)] * load_reps
-    for m in AWKWARD_M:
-        for l in LAYERS:
-            seq += [("m=%d" % m, l)] * awkward_reps
-    if graph:
+    seq = []
+    for s in range(warmup + steps):
         for name in LOAD_ORDER:
             for l in LAYERS:
-                seq += [(name, l)] * (1 + graph_reps)   # one direct warm-up run, then the replays
+                seq.append(("warmup" if s < warmup else name, l, LOADS[name]))
+    for _ in range(study_reps):
+        for cond, _, _ in STUDY_CONDITIONS:
+            seq.append(("study:" + cond, "pooler", 1))
+    for m in AWKWARD_M:
+        for l in LAYERS:
+            seq += [("m=%d" % m, l, m)] * awkward_reps
+    for name in LOAD_ORDER:
+        for _ in range(graph_reps):
+            seq += [("graph:" + name, l, LOADS[name]) for l in LAYERS]
     return seq
 
 
-def summarize_loads_trace(trace_csv, steps, warmup, load_reps, graph_reps, awkward_reps):
-    """Kernel durations of every (load, layer) from a rocprofv3 kernel trace of bench.py.
-
-    The projection launches in the trace (in start order) are matched one to
-    one with the launch sequence of the bench run; the run's step, warm-up and
-    repetition counts must be the ones given here.
-    """
+def summarize_loads_trace(trace_csv, steps, warmup, study_reps, awkward_reps, graph_reps):
+    """Kernel durations of every (tag, layer) from a rocprofv3 kernel trace of
+    bench.py, matching the trace's projection launches one to one with
+    call_sequence() (the run's counts must be the ones given here)."""
     from gemv_decode_projections_amd import roofline as rf
-    from workload import LOADS
 
     rows = sorted((r for r in _read_csv(trace_csv) if _is_proj_kernel(r["Kernel_Name"])),
                   key=lambda r: int(r["Start_Timestamp"]))
-    seq = call_sequence(steps, warmup, load_reps, graph_reps, awkward_reps)
+    seq = call_sequence(steps, warmup, study_reps, awkward_reps, graph_reps)
     if len(rows) != len(seq):
         raise SystemExit("trace has %d projection launches, the bench sequence %d: counts differ"
                          % (len(rows), len(seq)))
     per = {}
-    for (name, layer), r in zip(seq, rows):
-        e = per.setdefault((name, layer), {"kernel": r["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
-                                           "grid": int(r["Grid_Size_X"]), "d": []})
+    for (tag, layer, m), r in zip(seq, rows):
+        e = per.setdefault((tag, layer), {"kernel": _short(r["Kernel_Name"]), "m": m,
+                                          "grid": int(r["Grid_Size_X"]), "d": []})
+        if e["kernel"] != _short(r["Kernel_Name"]):
+            raise SystemExit("(%s, %s): launches of different kernels %s / %s" % (tag, layer, e["kernel"],
+                                                                                 _short(r["Kernel_Name"])))
         e["d"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    from workload import AWKWARD_M
-
     out = {}
-    for name in list(LOAD_ORDER) + ["m=%d" % m for m in AWKWARD_M]:
-        m = LOADS[name] if name in LOADS else int(name[2:])
-        lay = {}
-        for (n2, layer), e in per.items():
-            if n2 != name:
-                continue
-            med = statistics.median(e["d"])
-            lay[layer] = {"kernel": e["kernel"], "grid": e["grid"], "n": len(e["d"]), "median_us": round(med, 3),
-                          "TBps": round(rf.bytes_of(layer, m) / med / 1e6, 3),
-                          "TFLOPs": round(rf.flops_of(layer, m) / med / 1e6, 1)}
-        out[name] = {"m": m, "sum_median_us": round(sum(v["median_us"] for v in lay.values()), 2), "layers": lay}
+    for (tag, layer), e in per.items():
+        if tag == "warmup":
+            continue
+        d = out.setdefault(tag, {"m": e["m"], "layers": {}})
+        med = statistics.median(e["d"])
+        d["layers"][layer] = {"kernel": e["kernel"], "grid": e["grid"], "n": len(e["d"]),
+                              "median_us": round(med, 3), "mean_us": round(statistics.mean(e["d"]), 3),
+                              "TBps": round(rf.bytes_of(layer, e["m"]) / med / 1e6, 3)}
+    for d in out.values():
+        d["sum_median_us"] = round(sum(v["median_us"] for v in d["layers"].values()), 2)
     return out
 
+
+def summarize_graph_trace(trace_csv, graph_reps):
+    """In-graph kernel durations and the gaps between kernels, from the graph
+    replays of a rocprofv3 kernel trace of bench.py: each replayed graph is
+    a stamp kernel, five kernels, a stamp kernel. Per load (the load graphs
+    come in LOAD_ORDER, graph_reps each) and for the floor graphs: medians of
+    each kernel's duration, of the six gaps (stamp -> first kernel, the four
+    between kernels, last kernel -> stamp) and of the span from the first
+    kernel's start to the last one's end."""
+    rows = sorted(_read_csv(trace_csv), key=lambda r: int(r["Start_Timestamp"]))
+    stamps = [i for i, r in enumerate(rows) if "stamp_kernel" in r["Kernel_Name"]]
+    if len(stamps) % 2:
+        raise SystemExit("odd number of stamp kernels in the trace")
+    loads, floors = [], []
+    for a, b in zip(stamps[::2], stamps[1::2]):
+        inner = rows[a + 1:b]
+        if len(inner) != 5:
+            raise SystemExit("a stamped graph holds %d kernels, not 5" % len(inner))
+        ts = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in [rows[a]] + inner + [rows[b]]]
+        rec = {"kernels": [_short(r["Kernel_Name"]) for r in inner],
+               "dur": [(e - s) / 1e3 for s, e in ts[1:-1]],
+               "gaps": [(ts[i + 1][0] - ts[i][1]) / 1e3 for i in range(6)],
+               "span": (ts[5][1] - ts[1][0]) / 1e3}
+        (loads if all(_is_proj_kernel(k) for k in rec["kernels"]) else floors).append(rec)
+    if len(loads) != graph_reps * len(LOAD_ORDER) or len(floors) != len(loads):
+        raise SystemExit("found %d load and %d floor graph replays, expected %d each"
+                         % (len(loads), len(floors), graph_reps * len(LOAD_ORDER)))
+
+    def agg(recs):
+        return {"kernels": recs[0]["kernels"],
+                "kernel_median_us": [round(statistics.median(r["dur"][i] for r in recs), 3) for i in range(5)],
+                "gap_median_us": [round(statistics.median(r["gaps"][i] for r in recs), 3) for i in range(6)],
+                "span_median_us": round(statistics.median(r["span"] for r in recs), 3),
+                "n": len(recs)}
+    out = {}
+    for j, name in enumerate(LOAD_ORDER):
+        out[name] = {"graph": agg(loads[j * graph_reps:(j + 1) * graph_reps]),
+                     "floor_graph": agg(floors[j * graph_reps:(j + 1) * graph_reps])}
+    return out
+
+
+# ------------------------------------------------------- profile pages
 
 CMD_VARS = "`$REPO`: the repository root on the MI355X host; `$OUT`: the directory the runs write to"
 BENCH_CMD = "python3 $REPO/bench.py > $OUT/bench.json"
 PROFILE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_bench "
-               "-o bench -- python3 -u $REPO/bench.py --no-cpu-baseline")
+               "-o bench -- python3 -u $REPO/bench.py --no-cpu-baseline > $OUT/bench_prof.json")
 PMC_CMDS = (
     "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o fetch "
     "-- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_fetch.log 2>&1",
@@ -340,23 +473,6 @@ PMC_CMDS = (
     "-o mfma -- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_mfma.log 2>&1",
 )
 PMC_HASH_TAG = "pmc pass kernel sources:"
-
-
-def pass_source_hash(logs):
-    """The kernel-source hash the counter passes printed (every log must name
-    the same one): the counters belong to the sources that ran on the GPU, not
-    to whatever the tree holds when the summary is rendered."""
-    seen = set()
-    for path in logs:
-        with open(path) as f:
-            tags = [l.split(PMC_HASH_TAG, 1)[1].strip() for l in f if PMC_HASH_TAG in l]
-        if len(tags) != 1:
-            raise SystemExit("%s: expected one '%s' line, found %d" % (path, PMC_HASH_TAG, len(tags)))
-        seen.add(tags[0])
-    if len(seen) != 1:
-        raise SystemExit("the counter passes ran different kernel sources: %s" % sorted(seen))
-    return seen.pop()
-
 
 # With --out-root DIR, paths under DIR are shown as $OUT/... on the profile pages.
 OUT_ROOT = None
@@ -368,57 +484,60 @@ def shown(path):
     return path
 
 
-def md_decode1_trace(tr, trace_csv, bench_line=None, steps=50, warmup=5, bench_json=None):
-    """profiles/decode1_kernels_trace.md from summarize_trace()'s result (and,
-    when given, the JSON line of the same bench run without the profiler)."""
-    from gemv_decode_projections_amd import roofline as rf
-
-    L = ["# Decode-1 kernels: rocprofv3 kernel trace of bench.py (MI355X, 1 GPU)", "",
-         "Commands (%s):" % CMD_VARS, "", "```", BENCH_CMD, PROFILE_CMD,
-         "python bench.py --summarize-trace %s --md --bench-json %s > profiles/decode1_kernels_trace.md"
-         % (shown(trace_csv), shown(bench_json or "$OUT/bench.json")),
-         "python bench.py --summarize-loads-trace %s --md > profiles/loads_kernels_trace.md" % shown(trace_csv), "```", "",
-         "Timed region: the %d decode-1 steps after %d warmup steps (each call preceded by a 1 GiB flush)." % (steps, warmup),
-         "Kernel durations are the trace's start/end stamps."]
+def md_loads_trace(lt, trace_csv, counts, bench_line=None):
+    """profiles/loads_kernels_trace.md: every (load, layer) kernel's trace
+    durations, and the dominant kernel's event average from the same run."""
+    steps, warmup, study, awk, graph = counts
+    L = ["# Every load's kernels: rocprofv3 kernel trace of bench.py (MI355X, 1 GPU)", "",
+         "Commands (%s):" % CMD_VARS, "", "```", PROFILE_CMD,
+         "python bench.py --summarize-loads-trace %s --steps %d --warmup %d --study-reps %d --awkward-reps %d "
+         "--graph-reps %d --bench-json %s --md > profiles/loads_kernels_trace.md"
+         % (shown(trace_csv), steps, warmup, study, awk, graph, shown("$OUT/bench_prof.json")), "```", "",
+         "Every launch is cold (flush before it). Launches are matched in order with the bench's launch sequence",
+         "(`bench.call_sequence`); the load rows cover the %d timed steps; loads named m=<m> are the awkward token"
+         % steps,
+         "counts, graph:<load> the in-graph launches of the graph leg, study:<condition> the flush study's pooler",
+         "decode-1 calls. TB/s uses the algorithmic bytes (guide ch. 1 §1.7 formulas).", ""]
     if bench_line:
-        ev, roof = bench_line["decode1_layers_us"], bench_line["roofline"]
-        dom = roof["layer"]
-        L += ["The same bench command run without the profiler (and with the CPU baseline), in the same session,",
-              "reported (hipExtLaunchKernel events, median): " + ", ".join("%s %.2f" % (l, v) for l, v in ev.items())
-              + " us; dominant kernel %s (`%s`) event average %.3f us vs trace mean %.3f us." % (
-                  dom, roof["kernel"], roof["avg_us"], tr[dom]["mean_us"]),
-              "(Under the profiler the events themselves read longer per call, because tracing adds work around each",
-              "dispatch; the trace stamps do not include it.)"]
-        if roof.get("weights") == "12-bit lossless":
-            L += ["", "Kernels whose last template argument is `true` read 12-bit lossless weights; the dominant one (%s)"
-                  % dom, "reads %d bytes (%.3f of the BF16 bytes). Algorithmic bytes and GB/s below count the BF16 operation."
-                  % (roof["stored_bytes"], roof["stored_bytes"] / roof["algorithmic_bytes"])]
-    L += ["", "| layer | kernel | grid (threads) | n | mean us | median us | algorithmic bytes | GB/s (mean) |",
-          "|---|---|---|---|---|---|---|---|"]
-    for l, e in tr.items():
-        by = rf.bytes_of(l, 1)
-        L.append("| %s | `%s` | %d | %d | %.3f | %.3f | %d | %d |" % (l, e["kernel"], e["grid"], e["n"], e["mean_us"],
-                                                                     e["median_us"], by, round(by / e["mean_us"] / 1e3)))
-    L += ["", "Sum of the five trace medians: %.2f us per decode-1 load." % sum(e["median_us"] for e in tr.values()), ""]
+        roof = bench_line["roofline"]
+        tr = lt.get(roof["load"], {}).get("layers", {}).get(roof["layer"])
+        L += ["The bench line of the same profiled run reports the dominant kernel (%s, %s, `%s`) at an event"
+              % (roof["load"], roof["layer"], roof["kernel"]),
+              "average of %.3f us over the timed steps; the trace's mean for the same launches is %s us." % (
+                  roof["avg_us"], "%.3f" % tr["mean_us"] if tr else "n/a"), ""]
+    L += ["| load | m | layer | kernel | grid (threads) | n | median us | mean us | TB/s |",
+          "|---|---|---|---|---|---|---|---|---|"]
+    for ld, d in lt.items():
+        for l, e in d["layers"].items():
+            L.append("| %s | %d | %s | `%s` | %d | %d | %.3f | %.3f | %.3f |" % (
+                ld, d["m"], l, e["kernel"], e["grid"], e["n"], e["median_us"], e["mean_us"], e["TBps"]))
+    L += ["", "Per-load sums of the trace medians (us): "
+          + ", ".join("%s %.2f" % (ld, d["sum_median_us"]) for ld, d in lt.items() if ld in LOAD_ORDER) + ".", ""]
     return "\n".join(L)
 
 
-def md_loads_trace(lt, trace_csv):
-    """profiles/loads_kernels_trace.md from summarize_loads_trace()'s result."""
-    L = ["# Every load's kernels: rocprofv3 kernel trace of bench.py (MI355X, 1 GPU)", "",
-         "Same trace as `decode1_kernels_trace.md` (command there); table from",
-         "`python bench.py --summarize-loads-trace %s --md`." % shown(trace_csv),
-         "Every launch is cold (1 GiB flush before it). Launches are matched in order with the bench's launch",
-         "sequence (`bench.call_sequence`); n counts the event-timed calls, the graph warm-up run and the replays;",
-         "loads named m=<m> are the awkward token counts. TB/s and TFLOP/s use algorithmic bytes and FLOPs",
-         "(guide ch. 1 §1.7 formulas).", "",
-         "| load | m | layer | kernel | grid (threads) | n | median us | TB/s | TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
-    for ld, d in lt.items():
-        for l, e in d["layers"].items():
-            L.append("| %s | %d | %s | `%s` | %d | %d | %.3f | %.3f | %.1f |" % (
-                ld, d["m"], l, e["kernel"], e["grid"], e["n"], e["median_us"], e["TBps"], e["TFLOPs"]))
-    L += ["", "Per-load sums of the trace medians (us): "
-          + ", ".join("%s %.2f" % (ld, d["sum_median_us"]) for ld, d in lt.items()) + ".", ""]
+def md_graph_trace(gt, trace_csv, graph_reps):
+    """profiles/graph_replay_trace.md from summarize_graph_trace()."""
+    L = ["# Loads replayed as graphs: in-graph kernel durations and gaps (rocprofv3 kernel trace, MI355X)", "",
+         "Same profiled run as `loads_kernels_trace.md` (command there); table from",
+         "`python bench.py --summarize-graph-trace %s --graph-reps %d --md`." % (shown(trace_csv), graph_reps), "",
+         "Each load is one graph: a stamp kernel, the load's five projection kernels back to back (qkv_gate, o,",
+         "pooler, unpooler, router), a stamp kernel; its floor graph holds five read-floor kernels over the same",
+         "bytes. Every replay follows a flush; the two graphs alternate, order swapped each repetition.",
+         "Gaps: stamp -> first kernel, the four between kernels, last kernel -> stamp (start of the next minus end",
+         "of the previous, us). Span: first kernel start to last kernel end. Medians of %d replays." % graph_reps, "",
+         "| load | graph | kernel durations (us) | sum | gaps (us) | span us |", "|---|---|---|---|---|---|"]
+    for name, d in gt.items():
+        for which in ("graph", "floor_graph"):
+            e = d[which]
+            L.append("| %s | %s | %s | %.2f | %s | %.2f |" % (
+                name, "projections" if which == "graph" else "read floor",
+                " / ".join("%.2f" % v for v in e["kernel_median_us"]), sum(e["kernel_median_us"]),
+                " / ".join("%.2f" % v for v in e["gap_median_us"]), e["span_median_us"]))
+    inner = [g for d in gt.values() for g in d["graph"]["gap_median_us"][1:5]]
+    L += ["", "Between kernels of one graph the median gap is %.2f us (range %.2f-%.2f over the loads): the"
+          % (statistics.median(inner), min(inner), max(inner)),
+          "per-kernel fixed cost a load pays four times on top of its kernels' own durations.", ""]
     return "\n".join(L)
 
 
@@ -429,7 +548,7 @@ def md_pmc(pm, csvs, logs):
          "Commands (%s; one counter set per run):" % CMD_VARS, "", "```"] + list(PMC_CMDS) + [
          "python bench.py --summarize-pmc %s > profiles/pmc_loads.json" % args,
          "python bench.py --summarize-pmc %s --md > profiles/pmc_loads.md" % args, "```", "",
-         "The pass runs every load's five kernels cold (1 GiB flush before each), %d times, then copies 64 MiB three"
+         "The pass runs every load's five kernels cold (flush before each), %d times, then copies 64 MiB three"
          % PMC_REPS,
          "times. FETCH_SIZE reads %.4f x fewer KiB than that copy moves and WRITE_SIZE reads it with scale %.4f; both"
          % (pm["fetch_scale"], pm["write_scale"]),
@@ -452,6 +571,24 @@ def md_pmc(pm, csvs, logs):
     return "\n".join(L)
 
 
+def md_flush_study(line, bench_json):
+    """profiles/flush_study.md from a bench line's flush_study."""
+    fs = line["flush_study"]
+    L = ["# Which flush empties the caches: 67 MB read floor and pooler decode-1 (MI355X, 1 GPU)", "",
+         "Command (%s):" % CMD_VARS, "", "```", BENCH_CMD,
+         "python bench.py --flush-study-md %s > profiles/flush_study.md" % shown(bench_json), "```", "",
+         "Each condition is applied before every call (none: the call follows the previous call of the same",
+         "kernel, its data still cached); conditions interleaved, %d repetitions, medians of the kernels' own"
+         % fs["reps"],
+         "event durations. A flush that leaves the weights in the 256 MB Infinity Cache reads faster than one",
+         "that evicts them. The bench times every call after the `%s` flush." % fs["chosen"], "",
+         "| condition | 67.1 MB read floor (us) | pooler decode-1 kernel (us) |", "|---|---|---|"]
+    for c, v in fs["conditions"].items():
+        L.append("| %s | %.2f | %.2f |" % (c, v["floor_us"], v["pooler_decode1_us"]))
+    L.append("")
+    return "\n".join(L)
+
+
 PMC_REPS = 3
 
 
@@ -460,6 +597,22 @@ def pmc_sequence():
     from workload import LAYERS
 
     return [(name, l) for _ in range(PMC_REPS) for name in LOAD_ORDER for l in LAYERS]
+
+
+def pass_source_hash(logs):
+    """The kernel-source hash the counter passes printed (every log must name
+    the same one): the counters belong to the sources that ran on the GPU, not
+    to whatever the tree holds when the summary is rendered."""
+    seen = set()
+    for path in logs:
+        with open(path) as f:
+            tags = [l.split(PMC_HASH_TAG, 1)[1].strip() for l in f if PMC_HASH_TAG in l]
+        if len(tags) != 1:
+            raise SystemExit("%s: expected one '%s' line, found %d" % (path, PMC_HASH_TAG, len(tags)))
+        seen.add(tags[0])
+    if len(seen) != 1:
+        raise SystemExit("the counter passes ran different kernel sources: %s" % sorted(seen))
+    return seen.pop()
 
 
 def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20, sources=None):
@@ -490,7 +643,7 @@ def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20, sour
         m = LOADS[name]
         key = "%s@%d" % (layer, m)
         if key not in res["launches"]:
-            res["launches"][key] = {"load": name, "kernel": r["Kernel_Name"].split("(")[0].replace("void gdp::", ""),
+            res["launches"][key] = {"load": name, "kernel": _short(r["Kernel_Name"]),
                                     "grid": int(r["Grid_Size"]), "algorithmic_bytes": rf.bytes_of(layer, m)}
         return res["launches"][key]
 
@@ -532,31 +685,213 @@ def pmc_pass():
         b.kernel_us(layer, b.LOADS[name])
     torch.cuda.synchronize()
     for _ in range(3):
-        B.proj_bench_flush(b.flush, b.sink)
+        b.flush()
         B.proj_bench_copy(src, dst, n)
     torch.cuda.synchronize()
     log("pmc pass done: every load's kernels x%d, copy of %d bytes x3" % (PMC_REPS, n))
 
 
+# ------------------------------------------------------------------ main
+
+def run(args):
+    import torch
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    from gemv_decode_projections_amd import roofline as rf
+    from gemv_decode_projections_amd import binding as B
+
+    b = Bench()
+    layers = b.LAYERS
+    plans = {(name, l): B.proj_plan(l, b.LOADS[name]) for name in LOAD_ORDER for l in layers}
+    zcr = {l: B.proj_compressed(l) for l in layers}
+
+    # Warm-up steps (untimed), then the timed steps: every load once per step.
+    for _ in range(args.warmup):
+        for name in LOAD_ORDER:
+            for l in layers:
+                b.kernel_us(l, b.LOADS[name])
+    per = {(name, l): [] for name in LOAD_ORDER for l in layers}
+    step_us = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        tot = 0.0
+        for name in LOAD_ORDER:
+            for l in layers:
+                t = b.kernel_us(l, b.LOADS[name], variant=s % 2)
+                per[(name, l)].append(t)
+                tot += t
+        step_us.append(tot)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = statistics.median(step_us)
+    log("timed %d steps: %.2f us per step (median)" % (args.steps, value))
+
+    # Read floors over each shape's bytes (what its kernel reads), best of the
+    # read kernel's configurations with the projection kernel's own grid among them.
+    loads = {}
+    for name in LOAD_ORDER:
+        m = b.LOADS[name]
+        lay, fl, frac, tb, eff, cfgs = {}, {}, {}, {}, {}, {}
+        for l in layers:
+            cfg = plans[(name, l)]
+            t = statistics.median(per[(name, l)])
+            sb = stored_bytes(l, m, cfg, zcr[l])
+            f, fc = b.floor_us(sb, args.floor_reps, extra=((cfg.grid, min(cfg.block // 64, 16), 4),))
+            lay[l], fl[l] = round(t, 3), round(f, 3)
+            frac[l] = round(f / t, 3)
+            tb[l] = round(sb / t / 1e6, 3)
+            eff[l] = round(rf.bytes_of(l, m) / t / 1e6, 3)
+            cfgs[l] = {"kernel": kernel_name(cfg, l == "router"), "grid": cfg.grid, "block": cfg.block,
+                       "stored_bytes": sb, "floor_config": list(fc)}
+        tot = sum(lay.values())
+        loads[name] = {
+            "m": m, "us": round(tot, 2), "layers_us": lay, "read_floor_us": fl, "frac_of_read_floor": frac,
+            "read_floor_sum_us": round(sum(fl.values()), 2),
+            "TBps_read": tb, "TBps_bf16_equivalent": eff,
+            "TFLOPs": round(sum(rf.flops_of(l, m) for l in layers) / tot / 1e6, 2),
+            "nominal_floor_us": round(rf.load_floor_us(m, router_peak=rf.MI355X_FP32_FLOPS), 2),
+            "h200_best_us_context": H200_BEST_US[name],
+            "kernels": cfgs,
+        }
+        log("%-10s m=%-4d %8.2f us  %s" % (name, m, tot, lay))
+
+    # Flush study: 67 MB read floor and pooler decode-1 under each condition,
+    # conditions interleaved.
+    nb67 = rf.bytes_of("pooler", 1) // 16 * 16
+    _, fcfg = b.floor_us(nb67, args.floor_reps)
+    study = {c: {"floor": [], "pooler": []} for c, _, _ in STUDY_CONDITIONS}
+    for _ in range(args.study_reps):
+        for c, mode, nbytes in STUDY_CONDITIONS:
+            study[c]["floor"].append(b.floor_once(nb67, fcfg, flush=(mode, nbytes)))
+            study[c]["pooler"].append(b.kernel_us("pooler", 1, flush=(mode, nbytes)))
+    flush_study = {"reps": args.study_reps, "floor_config": list(fcfg), "floor_bytes": nb67,
+                   "chosen": next(c for c, mo, nb in STUDY_CONDITIONS if mo == FLUSH_MODE and nb == FLUSH_BYTES),
+                   "conditions": {c: {"floor_us": round(statistics.median(v["floor"]), 3),
+                                      "pooler_decode1_us": round(statistics.median(v["pooler"]), 3)}
+                                  for c, v in study.items()}}
+    log("flush study: %s" % flush_study["conditions"])
+
+    # The awkward token counts of the correctness sweep, timed the same way.
+    from workload import AWKWARD_M
+    awkward = {}
+    for m in AWKWARD_M:
+        lay = {l: round(statistics.median(b.kernel_us(l, m) for _ in range(args.awkward_reps)), 2) for l in layers}
+        awkward[str(m)] = {"us": round(sum(lay.values()), 2), "layers_us": lay}
+    log("awkward m: %s" % {m: v["us"] for m, v in awkward.items()})
+
+    # Graph leg: each load as one graph, paired and alternated with its floor graph.
+    khz = B.proj_bench_wallclock_khz()
+    graph = {"wallclock_khz": khz, "reps": args.graph_reps, "loads": {}}
+    for name in LOAD_ORDER:
+        m = b.LOADS[name]
+        gl, sl = b.load_graph(name)
+        gf, sf = b.floor_graph([stored_bytes(l, m, plans[(name, l)], zcr[l]) for l in layers])
+        raw = {"load": [], "floor": []}
+        span = {"load": [], "floor": []}
+        for r in range(args.graph_reps):
+            order = (("load", gl, sl), ("floor", gf, sf)) if r % 2 == 0 else (("floor", gf, sf), ("load", gl, sl))
+            for which, g, s in order:
+                raw[which].append(b.replay(g, s))
+                st = b.stamps[:4].cpu().tolist()
+                i0 = 0 if which == "load" else 2
+                span[which].append((st[i0 + 1] - st[i0]) * 1e3 / khz)
+        gd = {"stamped_span_us": round(statistics.median(span["load"]), 2),
+              "replay_event_us": round(statistics.median(raw["load"]), 2),
+              "floor_stamped_span_us": round(statistics.median(span["floor"]), 2),
+              "floor_replay_event_us": round(statistics.median(raw["floor"]), 2)}
+        gd["frac_of_floor_graph"] = round(gd["floor_stamped_span_us"] / gd["stamped_span_us"], 3)
+        graph["loads"][name] = gd
+        del gl, gf
+    graph["sum_stamped_span_us"] = round(sum(v["stamped_span_us"] for v in graph["loads"].values()), 2)
+    log("graph replay (stamped spans): %s" % {k: v["stamped_span_us"] for k, v in graph["loads"].items()})
+
+    # Roofline of the dominant kernel: the (load, layer) with the longest median time.
+    dom = max(per, key=lambda k: statistics.median(per[k]))
+    dname, dlayer = dom
+    dm = b.LOADS[dname]
+    dcfg = plans[dom]
+    d_avg = statistics.mean(per[dom])
+    d_stored = stored_bytes(dlayer, dm, dcfg, zcr[dlayer])
+    t_hbm = d_stored / 8e12
+    t_mfma = mfma_flops(dlayer, dm) / 2.5e15
+    kname = kernel_name(dcfg, dlayer == "router")
+    achieved = d_stored / d_avg / 1e3
+    roof = {
+        "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic_for(dlayer, dm, kname),
+        "load": dname, "layer": dlayer, "m": dm, "kernel": kname, "avg_us": round(d_avg, 3),
+        "bytes_per_launch": d_stored,
+        "bytes_rule": "W N_eff x K (x 3/4 plus the correction table on 12-bit weights) + x m x K x 2 + out m x N_eff "
+                      "x o, each once",
+        "effective_GBps": round(rf.bytes_of(dlayer, dm) / d_avg / 1e3, 1),
+        "mfma_TFLOPs": round(mfma_flops(dlayer, dm) / d_avg / 1e6, 1),
+        "mfma_frac": round(mfma_flops(dlayer, dm) / d_avg / 1e6 / MFMA_BF16_TFLOPS, 4),
+        "nominal_hbm_us": round(t_hbm * 1e6, 3), "nominal_mfma_us": round(t_mfma * 1e6, 3),
+        "measured_read_floor_us": loads[dname]["read_floor_us"][dlayer],
+    }
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(layers, b.LOADS)
+
+    h200_sum = sum(H200_BEST_US.values())
+    result = {
+        "metric": "cold-cache us per load (sum of 5 layers) + achieved HBM TB/s vs roofline, m=1-256",
+        "value": round(value, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(value / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(value / h200_sum, 4),
+        "baseline": {"value": round(h200_sum, 2), "unit": "us",
+                     "what": "sum of the pages' best per-load times on H200 SXM over the same six loads "
+                             "(guide ch. 1 §1.8; context from other hardware, not a target)"},
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "six loads, each the sum of five cold projections x @ W^T: decode-1 (m=1), decode-16 (m=16), "
+                        "decode-32 (m=32), verify-1 (m=8), verify-16 (m=128), verify-32 (m=256); layers qkv_gate "
+                        "2304x8192, o 8192x1024, pooler 4096x8192, unpooler 8192x4096 (rows 0-1023 at m<=8), "
+                        "router 256x8192 fp32 weights and output; x bf16",
+            "loads": {name: b.LOADS[name] for name in LOAD_ORDER},
+            "timing": "kernel duration from hipExtLaunchKernel start/stop events; %s flush of %d MiB before each call"
+                      % ("plain" if FLUSH_MODE else "non-temporal", FLUSH_BYTES >> 20),
+        },
+        "loads": loads,
+        "awkward_m": awkward,
+        "graph_replay": graph,
+        "flush_study": flush_study,
+        "timed_wall_s": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--load-reps", type=int, default=20, help="cold calls per layer for the other loads")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
-    ap.add_argument("--graph-reps", type=int, default=15)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--floor-reps", type=int, default=5, help="cold reads per floor configuration and shape")
+    ap.add_argument("--study-reps", type=int, default=15, help="repetitions of the flush study")
+    ap.add_argument("--graph-reps", type=int, default=21, help="cold replays per load graph (and floor graph)")
     ap.add_argument("--awkward-reps", type=int, default=7, help="cold calls per layer at each awkward token count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
-    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
-                    help="print per-layer durations of the timed steps from a rocprofv3 trace of bench.py")
     ap.add_argument("--summarize-loads-trace", metavar="KERNEL_TRACE_CSV",
                     help="print per-(load, layer) kernel durations from a rocprofv3 trace of bench.py")
+    ap.add_argument("--summarize-graph-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print in-graph kernel durations and gaps from a rocprofv3 trace of bench.py")
+    ap.add_argument("--flush-study-md", metavar="BENCH_JSON", help="print profiles/flush_study.md from a bench line")
     ap.add_argument("--md", action="store_true", help="with --summarize-*: print the profiles/ Markdown page")
-    ap.add_argument("--bench-json", metavar="PATH", help="with --summarize-trace --md: the bench line of the same run")
-    ap.add_argument("--out-root", metavar="DIR", help="with --md: show paths under DIR as $OUT/... (the runs' output directory)")
+    ap.add_argument("--bench-json", metavar="PATH", help="with --summarize-loads-trace --md: the line of the same run")
+    ap.add_argument("--out-root", metavar="DIR", help="with --md: show paths under DIR as $OUT/...")
     ap.add_argument("--pmc-logs", nargs="+", metavar="LOG",
                     help="with --summarize-pmc: the passes' output (names the kernel sources they ran)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
@@ -566,21 +901,25 @@ def main():
     global OUT_ROOT
     OUT_ROOT = args.out_root
 
-    if args.summarize_trace:
-        tr = summarize_trace(args.summarize_trace, args.steps, args.warmup)
-        if args.md:
-            line = None
-            if args.bench_json:
-                with open(args.bench_json) as f:
-                    line = json.loads(f.read().strip().splitlines()[-1])
-            print(md_decode1_trace(tr, args.summarize_trace, line, args.steps, args.warmup, args.bench_json))
-        else:
-            print(json.dumps(tr, indent=1))
-        return
+    def last_line(path):
+        with open(path) as f:
+            return json.loads(f.read().strip().splitlines()[-1])
+
     if args.summarize_loads_trace:
-        lt = summarize_loads_trace(args.summarize_loads_trace, args.steps, args.warmup, args.load_reps,
-                                   args.graph_reps, args.awkward_reps)
-        print(md_loads_trace(lt, args.summarize_loads_trace) if args.md else json.dumps(lt, indent=1))
+        counts = (args.steps, args.warmup, args.study_reps, args.awkward_reps, args.graph_reps)
+        lt = summarize_loads_trace(args.summarize_loads_trace, *counts)
+        if args.md:
+            line = last_line(args.bench_json) if args.bench_json else None
+            print(md_loads_trace(lt, args.summarize_loads_trace, counts, line))
+        else:
+            print(json.dumps(lt, indent=1))
+        return
+    if args.summarize_graph_trace:
+        gt = summarize_graph_trace(args.summarize_graph_trace, args.graph_reps)
+        print(md_graph_trace(gt, args.summarize_graph_trace, args.graph_reps) if args.md else json.dumps(gt, indent=1))
+        return
+    if args.flush_study_md:
+        print(md_flush_study(last_line(args.flush_study_md), args.flush_study_md))
         return
     if args.summarize_pmc:
         if len(args.summarize_pmc) not in (2, 3):
@@ -597,147 +936,7 @@ def main():
     if args.pmc_pass:
         pmc_pass()
         return
-
-    import torch
-
-    if not torch.cuda.is_available():
-        sys.exit("bench.py needs a GPU")
-    from gemv_decode_projections_amd import roofline as rf
-    from gemv_decode_projections_amd import binding as B
-    from gemv_decode_projections_amd import layers as layers_mod
-
-    b = Bench()
-    layers = b.LAYERS
-
-    # Warmup steps (untimed).
-    for _ in range(args.warmup):
-        for layer in layers:
-            b.kernel_us(layer, 1)
-
-    # Timed steps: one decode-1 load each.
-    per_layer = {l: [] for l in layers}
-    step_us = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        tot = 0.0
-        for layer in layers:
-            t = b.kernel_us(layer, 1, variant=s % 2)
-            per_layer[layer].append(t)
-            tot += t
-        step_us.append(tot)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    value = statistics.median(step_us)
-
-    # Read floor at each layer's byte count, and the other loads.
-    floor = {l: b.floor_us(rf.bytes_of(l, 1), 15) for l in layers}
-    loads = {}
-    for name in LOAD_ORDER:
-        m = b.LOADS[name]
-        lay = {}
-        for layer in layers:
-            if name == "decode-1":
-                t = statistics.median(per_layer[layer])
-            else:
-                t = statistics.median(b.kernel_us(layer, m, variant=r % 2) for r in range(args.load_reps))
-            lay[layer] = round(t, 2)
-        tot = sum(lay.values())
-        nbytes = sum(rf.bytes_of(l, m) for l in layers)
-        flops = sum(rf.flops_of(l, m) for l in layers)
-        # The hand-written read kernel over each shape's algorithmic bytes.
-        lfloor = {l: floor[l] if m == 1 else b.floor_us(rf.bytes_of(l, m), 9) for l in layers}
-        loads[name] = {
-            "m": m, "us": round(tot, 2), "layers_us": lay,
-            "read_floor_us": {l: round(v, 2) for l, v in lfloor.items()},
-            "frac_of_read_floor": {l: round(lfloor[l] / lay[l], 3) for l in layers},
-            "TBps": round(nbytes / tot / 1e6, 3),
-            "TFLOPs": round(flops / tot / 1e6, 2),
-            "mfma_frac": round(flops / tot / 1e6 / MFMA_BF16_TFLOPS, 4),
-            "nominal_floor_us": round(rf.load_floor_us(m, router_peak=rf.MI355X_FP32_FLOPS), 2),
-        }
-        log("%-10s m=%-4d %8.2f us  %s" % (name, m, tot, lay))
-
-    # The awkward token counts of the correctness sweep, timed the same way
-    # (cold, kernel-duration events): per layer and summed over the five.
-    from workload import AWKWARD_M
-    awkward = {}
-    for m in AWKWARD_M:
-        lay = {l: round(statistics.median(b.kernel_us(l, m) for _ in range(args.awkward_reps)), 2) for l in layers}
-        awkward[str(m)] = {"us": round(sum(lay.values()), 2), "layers_us": lay}
-    log("awkward m: %s" % {m: v["us"] for m, v in awkward.items()})
-
-    # The pages' own timing method for context: each call captured in a HIP
-    # graph and replayed cold, minus the same for a graph of one empty kernel.
-    graph = None
-    if not args.no_graph:
-        empty = b.graph_us(None, 1, args.graph_reps)
-        graph = {"empty_graph_us": round(empty, 2), "loads": {}}
-        for name in LOAD_ORDER:
-            m = b.LOADS[name]
-            lay = {l: round(b.graph_us(l, m, args.graph_reps) - empty, 2) for l in layers}
-            graph["loads"][name] = {"m": m, "us_net": round(sum(lay.values()), 2), "layers_net_us": lay}
-        log("graph replay (net of an empty-kernel graph, %.2f us): %s" % (
-            empty, {k: v["us_net"] for k, v in graph["loads"].items()}))
-
-    # Roofline of the dominant kernel of the headline load.
-    dom = max(layers, key=lambda l: statistics.median(per_layer[l]))
-    dom_avg = statistics.mean(per_layer[dom])
-    dom_bytes = rf.bytes_of(dom, 1)
-    achieved = dom_bytes / dom_avg / 1e3  # GB/s
-    cfg = B.proj_plan(dom, 1)
-    kname = kernel_name(cfg, dom == "router")
-    # With 12-bit weights the kernel reads 3/4 of the BF16 weight bytes plus
-    # one correction table; "achieved" still counts the BF16 bytes the
-    # operation is defined on, and stored_bytes says what is actually read.
-    stored = dom_bytes
-    if cfg.kind == 0 and cfg.flags & 4:
-        n, k, _, _ = layers_mod.DIMS[dom]
-        stored = dom_bytes - rf.weight_bytes(dom, 1) // 4 + n * B.proj_compressed(dom) * 8
-    roof = {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-        "stored_bytes": stored, "weights": "12-bit lossless" if stored != dom_bytes else "bf16" if dom != "router" else "fp32",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dom, 1, kname),
-        "kernel": kname, "layer": dom, "algorithmic_bytes": dom_bytes, "avg_us": round(dom_avg, 3),
-        "measured_read_floor_us": round(floor[dom], 3),
-        "frac_of_read_floor": round(floor[dom] / statistics.median(per_layer[dom]), 4),
-    }
-
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
-
-    floor_sum = sum(floor.values())
-    result = {
-        "metric": "cold-cache us per load (sum of 5 layers) + achieved HBM TB/s vs roofline, m=1-256",
-        "value": round(value, 3),
-        "unit": "us",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(value / 1e3, 6),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": round(value / H200_DECODE1_US, 4),
-        "baseline": {"value": H200_DECODE1_US, "unit": "us", "what": "pages' best decode-1 load time on H200 SXM (context, other hardware)"},
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "decode-1 load: m=1 through qkv_gate 2304x8192, o 8192x1024, pooler 4096x8192, "
-                        "unpooler rows 0-1023 of 8192x4096, router 256x8192 fp32; cold cache before each layer",
-            "m": 1,
-            "timing": "kernel duration from hipExtLaunchKernel start/stop events, 1 GiB read flush before each call",
-        },
-        "decode1_layers_us": {l: round(statistics.median(per_layer[l]), 3) for l in layers},
-        "decode1_read_floor_us": {l: round(floor[l], 3) for l in layers},
-        "decode1_frac_of_read_floor": round(floor_sum / value, 4),
-        "decode1_TBps": round(sum(rf.bytes_of(l, 1) for l in layers) / value / 1e6, 3),
-        "loads": loads,
-        "awkward_m": awkward,
-        "graph_replay": graph,
-        "timed_wall_s": round(wall, 4),
-        "roofline": roof,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(result), flush=True)
+    run(args)
 
 
 if __name__ == "__main__":
