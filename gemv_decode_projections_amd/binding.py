@@ -24,6 +24,7 @@ STATUS = {
     -6: "PROJ_ERR_UNSUPPORTED",
     -7: "PROJ_ERR_HIP",
     -8: "PROJ_ERR_DEVICE",
+    -9: "PROJ_ERR_SCRATCH",
 }
 
 
@@ -67,6 +68,7 @@ def _lib():
     sig = {
         "proj_prepare": ([i, vp], i),
         "proj_run": ([i, vp, i, vp, vp], i),
+        "proj_run_noalloc": ([i, vp, i, vp, vp], i),
         "proj_out_cols": ([i, i], i),
         "proj_layer_dims": ([i, ip, ip, ip, ip], i),
         "proj_release": ([i], i),
@@ -186,6 +188,13 @@ def proj_run(layer, x, m, out, stream=None):
     _check_io(layer, x, m, out)
     _check(_lib().proj_run(_layers.layer_id(layer), _ptr(x), int(m), _ptr(out), _stream(stream)),
            "proj_run(%s, m=%d)" % (_layers.layer_name(layer), m))
+
+
+def proj_run_noalloc(layer, x, m, out, stream=None):
+    """proj_run with the split-K scratch in the library's fixed device array (allocates nothing)."""
+    _check_io(layer, x, m, out)
+    _check(_lib().proj_run_noalloc(_layers.layer_id(layer), _ptr(x), int(m), _ptr(out), _stream(stream)),
+           "proj_run_noalloc(%s, m=%d)" % (_layers.layer_name(layer), m))
 
 
 def proj_run_config(layer, x, m, out, cfg, stream=None):

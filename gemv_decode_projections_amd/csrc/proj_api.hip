@@ -16,6 +16,18 @@
 #include "variants.h"
 #include "wide.h"
 
+// Split-K scratch of proj_run_noalloc, for callers that cannot allocate: one
+// fixed array in the library's device image, so each GPU holds its own copy
+// until the process ends. Regions, in order: polled partials (every word all
+// ones between launches), counted partials, arrival counters (zero between
+// launches). Host code never passes this name to a kernel: it stands for a
+// host-side shadow; the device address comes from hipGetSymbolAddress.
+constexpr size_t kScratchPolled = 4u << 20;
+constexpr size_t kScratchCounted = 16u << 20;
+constexpr size_t kScratchCounters = 1u << 14;
+constexpr size_t kScratchBytes = kScratchPolled + kScratchCounted + kScratchCounters * sizeof(uint32_t);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace gdp {
 namespace {
 
@@ -70,12 +82,19 @@ struct LayerState {
     int zcr = -1;                 // slots per row; -1: no 12-bit form
     uint32_t zt0 = 0, zt1 = 0;    // exponent table
     uint32_t *giveups = nullptr;  // polled split-K: reducer give-ups since prepare / last reset
+    size_t ws_bytes = kWsBytes;   // capacity of ws
+    size_t pws_bytes = kWsBytes;  // capacity of pws
+    size_t n_counters = kCounters;
     int device = -1;
     bool prepared = false;
 };
 
 LayerState g_layers[PROJ_NUM_LAYERS];
 int g_last_hip = 0;
+
+// Device address of `scratch` on each GPU (set once per device by prepare).
+constexpr int kMaxDevices = 64;
+void *g_scratch[kMaxDevices] = {};
 
 int hip_fail(hipError_t e)
 {
@@ -206,7 +225,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
             return PROJ_ERR_UNSUPPORTED;
         if (c.ksplit > 1) {
             const long long elems = (long long)c.rb * c.nt * kWave;
-            if ((long long)n_rt * n_tt * c.ksplit * elems * (long long)sizeof(f32x4) > (long long)kWsBytes)
+            if ((long long)n_rt * n_tt * c.ksplit * elems * (long long)sizeof(f32x4) > (long long)st.pws_bytes)
                 return PROJ_ERR_UNSUPPORTED;
         }
         L.fn = v->fn;
@@ -251,9 +270,9 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
             return PROJ_ERR_UNSUPPORTED;
         if (c.ksplit > 1) {
             const long long tile_bytes = (long long)c.rb * c.nt * kWave * 16;
-            if ((long long)n_rt * n_tt * c.ksplit * tile_bytes > (long long)kWsBytes)
+            if ((long long)n_rt * n_tt * c.ksplit * tile_bytes > (long long)st.ws_bytes)
                 return PROJ_ERR_UNSUPPORTED;
-            if ((long long)n_rt * n_tt > (long long)kCounters)
+            if ((long long)n_rt * n_tt > (long long)st.n_counters)
                 return PROJ_ERR_UNSUPPORTED;
         }
         L.fn = v->fn;
@@ -312,9 +331,9 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
             return PROJ_ERR_UNSUPPORTED;
         if (slots > 1) {
             const long long tile_bytes = (long long)c.rb * c.nt * kWave * 16;
-            if (tiles * slots * tile_bytes > (long long)kWsBytes)
+            if (tiles * slots * tile_bytes > (long long)st.ws_bytes)
                 return PROJ_ERR_UNSUPPORTED;
-            if (tiles > (long long)kCounters)
+            if (tiles > (long long)st.n_counters)
                 return PROJ_ERR_UNSUPPORTED;
         }
         L.fn = stream ? v->fn_stream : v->fn;
@@ -325,7 +344,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
         A.wp = st.wp;
         A.zrow = st.zrow;
         A.ws = reinterpret_cast<float *>(st.ws);
-        A.ws_bytes = (uint32_t)kWsBytes;
+        A.ws_bytes = (uint32_t)st.ws_bytes;
         A.counters = st.counters;
         A.m = m;
         A.K = li.K;
@@ -672,6 +691,45 @@ void free_layer(LayerState &st)
     st = LayerState{};
 }
 
+// Once per device, with that device current: the device address of the
+// fixed scratch array, its polled region filled with the empty marks and the
+// counters zeroed (the only writes to it outside the kernels themselves).
+int scratch_setup(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return PROJ_ERR_DEVICE;
+    if (g_scratch[dev])
+        return PROJ_OK;
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (!p)
+        return PROJ_ERR_NULL;
+    if ((e = hipMemset(p, 0xff, kScratchPolled)) != hipSuccess ||
+        (e = hipMemset(static_cast<char *>(p) + kScratchPolled + kScratchCounted, 0,
+                       kScratchCounters * sizeof(uint32_t))) != hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess)
+        return hip_fail(e);
+    g_scratch[dev] = p;
+    return PROJ_OK;
+}
+
+// The layer state with its split-K workspaces replaced by the device's fixed
+// scratch (capacities reduced to the scratch's regions).
+LayerState with_scratch(const LayerState &st, void *p)
+{
+    LayerState v = st;
+    char *b = static_cast<char *>(p);
+    v.pws = reinterpret_cast<uint64_t *>(b);
+    v.pws_bytes = kScratchPolled;
+    v.ws = reinterpret_cast<f32x4 *>(b + kScratchPolled);
+    v.ws_bytes = kScratchCounted;
+    v.counters = reinterpret_cast<uint32_t *>(b + kScratchPolled + kScratchCounted);
+    v.n_counters = kScratchCounters;
+    return v;
+}
+
 // Launches every kernel the dispatch table can pick for the layer once (guide
 // ch. 10 "Measure, experiment, and try your own changes", Experiment D: an
 // unsupported configuration shows up in prepare's warm-up, never in a timed
@@ -737,6 +795,9 @@ int proj_prepare(int layer, const void *W)
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return hip_fail(e);
+    int rs = scratch_setup(dev);
+    if (rs)
+        return rs;
     // The new state is built, repacked and warmed up next to the old one,
     // which stays usable until the new one is complete.
     const size_t wbytes = (size_t)li.N * li.K * li.w_bytes;
@@ -803,6 +864,25 @@ int proj_run(int layer, const void *x, int m, void *out, void *stream)
     rc = resolve(layer, m, c, L, g_layers[layer]);
     if (rc)
         return rc;
+    return launch(L, x, out, static_cast<hipStream_t>(stream));
+}
+
+int proj_run_noalloc(int layer, const void *x, int m, void *out, void *stream)
+{
+    int rc = check_run_args(layer, x, m, out);
+    if (rc)
+        return rc;
+    const LayerState &st = g_layers[layer];
+    void *p = (st.device >= 0 && st.device < kMaxDevices) ? g_scratch[st.device] : nullptr;
+    if (!p)
+        return PROJ_ERR_NOT_PREPARED;
+    proj_config c = plan_default(layer, m, st.zcr);
+    Launch L;
+    if ((rc = resolve(layer, m, c, L, st)) != PROJ_OK)
+        return rc;
+    // The same plan over the fixed scratch: only its capacity can refuse it.
+    if (resolve(layer, m, c, L, with_scratch(st, p)) != PROJ_OK)
+        return PROJ_ERR_SCRATCH;
     return launch(L, x, out, static_cast<hipStream_t>(stream));
 }
 
@@ -895,6 +975,7 @@ const char *proj_strerror(int status)
     case PROJ_ERR_UNSUPPORTED: return "kernel configuration not compiled or does not tile the layer";
     case PROJ_ERR_HIP: return "HIP runtime error";
     case PROJ_ERR_DEVICE: return "current device differs from the layer's device";
+    case PROJ_ERR_SCRATCH: return "the plan's split-K partials exceed the fixed scratch of proj_run_noalloc";
     default: return "unknown status";
     }
 }
@@ -996,8 +1077,11 @@ int proj_split_giveups(int layer, int reset)
         return hip_fail(e);
     if (reset) {
         // A partial published after its reducer gave up would read as
-        // arrived in a later launch: restore every mark, then the count.
-        if ((e = hipMemset(st.pws, 0xff, kWsBytes)) != hipSuccess ||
+        // arrived in a later launch: restore every mark (the layer's
+        // workspace and the device's fixed scratch), then the count.
+        void *p = (st.device >= 0 && st.device < kMaxDevices) ? g_scratch[st.device] : nullptr;
+        if ((p && (e = hipMemset(p, 0xff, kScratchPolled)) != hipSuccess) ||
+            (e = hipMemset(st.pws, 0xff, kWsBytes)) != hipSuccess ||
             (e = hipMemset(st.giveups, 0, sizeof n)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess)
             return hip_fail(e);
     }

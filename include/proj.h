@@ -56,7 +56,8 @@ enum proj_status {
     PROJ_ERR_NOT_PREPARED = -5, /* proj_run before proj_prepare for that layer */
     PROJ_ERR_UNSUPPORTED = -6,  /* a requested kernel configuration is not built */
     PROJ_ERR_HIP = -7,          /* a HIP runtime call failed (see proj_last_hip_error) */
-    PROJ_ERR_DEVICE = -8        /* current device differs from the one the layer was prepared on */
+    PROJ_ERR_DEVICE = -8,       /* current device differs from the one the layer was prepared on */
+    PROJ_ERR_SCRATCH = -9       /* proj_run_noalloc: the plan needs more split-K scratch than it has */
 };
 
 /*
@@ -113,6 +114,26 @@ int proj_prepare(int layer, const void *W);
  *    PROJ_ERR_HIP if the launch is rejected.
  */
 int proj_run(int layer, const void *x, int m, void *out, void *stream);
+
+/*
+ * proj_run_noalloc - proj_run for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, plan, kernels and results as proj_run; the
+ * split-K partials and arrival counters live in one fixed device array of the
+ * library (4 MiB of polled partials, 16 MiB of counted partials, 16384
+ * counters; each GPU holds its own copy until the process ends), set up by the
+ * first proj_prepare on that device. Allocates nothing and calls no
+ * allocating routine. The kernels restore the array's empty marks and zeroed
+ * counters themselves; every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU race (a single stream, or calls ordered between
+ * streams, is safe); proj_run calls use the layer's own workspace and do not
+ * interfere. A reducer give-up is counted for proj_split_giveups(layer), whose
+ * reset also restores the array's marks.
+ * Errors: those of proj_run, and PROJ_ERR_SCRATCH when (layer, m)'s plan needs
+ * more partials or counters than the array holds (for instance the router past
+ * 1024 tokens); nothing is launched then.
+ */
+int proj_run_noalloc(int layer, const void *x, int m, void *out, void *stream);
 
 /*
  * proj_out_cols - columns of out: N, except 1024 for the unpooler at m <= 8
