@@ -388,23 +388,25 @@ proj_config plan_default(int layer, int m, int zcr)
     struct Entry {
         int nt, rb, waves, spw, ksplit, z;   // z: read the 12-bit weights when the layer has them
     };
-    // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32. The 12-bit
-    // form pays where the weight stream is long and one pass over it covers
-    // the tokens (qkv_gate and pooler up to 16 tokens, the full unpooler at
-    // 9-16); o measured slower (a short stream, where the correction wave
-    // and epilogue pass do not hide), and past 16 tokens the BF16 kernels'
-    // wider workgroups win.
+    // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32. Entries
+    // are the fastest of every compiled configuration in cold sweeps (a plain
+    // 1 GiB read before each call, so no weight byte is left in L2 or the
+    // Infinity Cache), kept where they beat the next one by more than the
+    // sweep's noise. The 12-bit form pays wherever the weight stream is long
+    // (qkv_gate, pooler, the full unpooler; up to 32 tokens, where 32-row
+    // workgroups read it once for one or two 16-token blocks); o's short
+    // stream does not hide the correction wave.
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {2, 2, 4, 32, 2, 0}},
+        {{1, 1, 8, 32, 1, 1}, {1, 2, 8, 16, 2, 1}, {1, 2, 8, 32, 1, 1}},
         /* o         512 row blocks,  32 k-steps */
-        {{1, 2, 4, 8, 1, 0}, {1, 2, 4, 8, 1, 0}, {2, 2, 4, 8, 1, 0}},
+        {{1, 2, 8, 4, 1, 0}, {1, 2, 8, 4, 1, 0}, {2, 2, 4, 8, 1, 0}},
         /* pooler    256 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {1, 2, 16, 16, 1, 0}},
+        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {1, 2, 8, 32, 1, 1}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
-        {{1, 1, 8, 16, 1, 0}, {1, 2, 8, 16, 1, 1}, {2, 2, 4, 32, 1, 0}},
+        {{1, 1, 4, 8, 4, 0}, {1, 2, 8, 16, 1, 1}, {2, 2, 4, 32, 1, 1}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
-        {{1, 1, 8, 4, 8, 0}, {1, 1, 8, 4, 8, 0}, {1, 1, 8, 4, 8, 0}},
+        {{1, 1, 8, 4, 8, 0}, {1, 1, 16, 2, 8, 0}, {1, 1, 16, 2, 8, 0}},
     };
     proj_config c{};
     // Few tokens on the router (m <= 8) and the unpooler slice (m <= 4):
@@ -481,13 +483,15 @@ proj_config plan_default(int layer, int m, int zcr)
     // far slower: qkv_gate m = 130 with 64-token tiles took 18.7 us at 4
     // splits, 216 workgroups, 32.4 at 5, 270 workgroups, and 24.5 at 3).
     struct TEntry {
-        int kind, rb, nt, depth, ksplit;
+        int kind, rb, nt, waves, depth, ksplit;
     };
+    // Measured in the same cold sweeps (m = 64, 128, 256); bucket 3 (past 256
+    // tokens) keeps its split rule below.
     static const TEntry ttable[PROJ_ROUTER][4] = {   // the four BF16 layers
-        /* qkv_gate */ {{3, 4, 2, 8, 3}, {3, 4, 4, 8, 3}, {3, 8, 4, 8, 0}, {3, 8, 4, 16, 0}},
-        /* o        */ {{1, 4, 2, 8, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 4, 0}, {3, 8, 4, 4, 0}},
-        /* pooler   */ {{3, 8, 2, 8, 3}, {3, 8, 4, 8, 4}, {3, 8, 4, 16, 0}, {3, 8, 4, 16, 0}},
-        /* unpooler */ {{1, 4, 2, 16, 1}, {1, 8, 2, 8, 1}, {3, 8, 4, 16, 0}, {3, 8, 4, 16, 0}},
+        /* qkv_gate */ {{3, 4, 4, 4, 16, 6}, {3, 4, 4, 4, 16, 3}, {3, 8, 4, 4, 16, 0}, {3, 8, 4, 4, 16, 0}},
+        /* o        */ {{1, 4, 2, 4, 16, 1}, {1, 8, 2, 4, 8, 1}, {3, 8, 4, 4, 4, 0}, {3, 8, 4, 4, 4, 0}},
+        /* pooler   */ {{3, 4, 4, 4, 8, 4}, {3, 8, 4, 4, 8, 4}, {3, 8, 8, 8, 8, 0}, {3, 8, 4, 4, 16, 0}},
+        /* unpooler */ {{1, 4, 2, 4, 16, 1}, {3, 4, 4, 4, 16, 1}, {3, 8, 4, 4, 16, 0}, {3, 8, 4, 4, 16, 0}},
     };
     const int ne = n_eff_of(layer, m);
     // Past 256 tokens the 8-wave wide kernel (two waves per SIMD) holds
@@ -543,7 +547,7 @@ proj_config plan_default(int layer, int m, int zcr)
     c.kind = e.kind;
     c.rb = e.rb;
     c.nt = e.nt;
-    c.waves = 4;
+    c.waves = e.waves;
     c.spw = e.depth;
     const long n_rt = ne / (16 * c.rb);
     if (m > 256 && n_rt * ((m + 63) / 64) > 256) {

@@ -99,8 +99,11 @@ def test_dispatch_plans_tile_every_layer(lib):
                 # wide tiles: 4 waves (8 past 256 tokens, 256-row tiles), whole row blocks per
                 # wave, any split up to one super-step each
                 assert cfg.kind == 3 and m > 32 and cfg.waves in (4, 8) and cfg.rb % cfg.waves == 0
+                # 8 waves: 256-row tiles past 256 tokens and for the pooler at 129-192; 128-row
+                # tiles (one row block per wave) for the pooler at 193-256
                 assert cfg.waves == 4 or (cfg.rb == 16 and (m > 256 and cfg.nt in (4, 8) or
-                                                             name == "pooler" and 128 < m <= 192 and cfg.nt == 4))
+                                                             name == "pooler" and 128 < m <= 192 and cfg.nt == 4)) \
+                    or (name == "pooler" and 64 < m <= 256 and cfg.rb == 8)
                 assert 1 <= cfg.ksplit <= k // (128 if cfg.spw >= 16 else 64)
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
