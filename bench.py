@@ -363,7 +363,7 @@ def _read_csv(path):
 def call_sequence(steps, warmup, study_reps, awkward_reps, graph_reps):
     """(tag, layer, m) of every projection kernel bench.py launches, in launch
     order: the event-timed steps (tag = load name, warm-up steps tagged
-    'warmup'), the flush study's pooler calls ('study:<condition>'), the
+    'warmup:<load>'), the flush study's pooler calls ('study:<condition>'), the
     awkward token counts ('m=<m>') and the graph replays ('graph:<load>')."""
     from workload import AWKWARD_M, LAYERS, LOADS
 
@@ -371,7 +371,7 @@ def call_sequence(steps, warmup, study_reps, awkward_reps, graph_reps):
     for s in range(warmup + steps):
         for name in LOAD_ORDER:
             for l in LAYERS:
-                seq.append(("warmup" if s < warmup else name, l, LOADS[name]))
+                seq.append(("warmup:" + name if s < warmup else name, l, LOADS[name]))
     for _ in range(study_reps):
         for cond, _, _ in STUDY_CONDITIONS:
             seq.append(("study:" + cond, "pooler", 1))
@@ -390,7 +390,11 @@ def summarize_loads_trace(trace_csv, steps, warmup, study_reps, awkward_reps, gr
     call_sequence() (the run's counts must be the ones given here)."""
     from gemv_decode_projections_amd import roofline as rf
 
-    rows = sorted((r for r in _read_csv(trace_csv) if _is_proj_kernel(r["Kernel_Name"])),
+    allrows = _read_csv(trace_csv)
+    # proj_prepare's warm-up launches come before the bench's first flush.
+    flushes = [int(r["Start_Timestamp"]) for r in allrows if "flush_kernel" in r["Kernel_Name"]]
+    t_first = min(flushes) if flushes else -1
+    rows = sorted((r for r in allrows if _is_proj_kernel(r["Kernel_Name"]) and int(r["Start_Timestamp"]) > t_first),
                   key=lambda r: int(r["Start_Timestamp"]))
     seq = call_sequence(steps, warmup, study_reps, awkward_reps, graph_reps)
     if len(rows) != len(seq):
@@ -406,7 +410,7 @@ def summarize_loads_trace(trace_csv, steps, warmup, study_reps, awkward_reps, gr
         e["d"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     out = {}
     for (tag, layer), e in per.items():
-        if tag == "warmup":
+        if tag.startswith("warmup"):
             continue
         d = out.setdefault(tag, {"m": e["m"], "layers": {}})
         med = statistics.median(e["d"])
@@ -492,7 +496,7 @@ def md_loads_trace(lt, trace_csv, counts, bench_line=None):
          "Commands (%s):" % CMD_VARS, "", "```", PROFILE_CMD,
          "python bench.py --summarize-loads-trace %s --steps %d --warmup %d --study-reps %d --awkward-reps %d "
          "--graph-reps %d --bench-json %s --md > profiles/loads_kernels_trace.md"
-         % (shown(trace_csv), steps, warmup, study, awk, graph, shown("$OUT/bench_prof.json")), "```", "",
+         % (shown(trace_csv), steps, warmup, study, awk, graph, shown("$OUT/bench.json")), "```", "",
          "Every launch is cold (flush before it). Launches are matched in order with the bench's launch sequence",
          "(`bench.call_sequence`); the load rows cover the %d timed steps; loads named m=<m> are the awkward token"
          % steps,
@@ -501,10 +505,13 @@ def md_loads_trace(lt, trace_csv, counts, bench_line=None):
     if bench_line:
         roof = bench_line["roofline"]
         tr = lt.get(roof["load"], {}).get("layers", {}).get(roof["layer"])
-        L += ["The bench line of the same profiled run reports the dominant kernel (%s, %s, `%s`) at an event"
-              % (roof["load"], roof["layer"], roof["kernel"]),
-              "average of %.3f us over the timed steps; the trace's mean for the same launches is %s us." % (
-                  roof["avg_us"], "%.3f" % tr["mean_us"] if tr else "n/a"), ""]
+        L += ["The same bench command run without the profiler in the same session (`%s`) reports the dominant kernel"
+              % BENCH_CMD,
+              "(%s, %s, `%s`) at an event average of %.3f us over its timed steps; the trace's mean for the same"
+              % (roof["load"], roof["layer"], roof["kernel"], roof["avg_us"]),
+              "launches is %s us. (Under the profiler the events themselves read longer per call, because tracing"
+              % ("%.3f" % tr["mean_us"] if tr else "n/a"),
+              "adds work around each dispatch; the trace stamps do not include it.)", ""]
     L += ["| load | m | layer | kernel | grid (threads) | n | median us | mean us | TB/s |",
           "|---|---|---|---|---|---|---|---|---|"]
     for ld, d in lt.items():
@@ -634,7 +641,9 @@ def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20, sour
     def launches(path, cname):
         rows = sorted((r for r in _read_csv(path) if r["Counter_Name"] == cname),
                       key=lambda r: int(r["Dispatch_Id"]))
-        sk = [r for r in rows if _is_proj_kernel(r["Kernel_Name"])]
+        # proj_prepare's warm-up launches come before the pass's first flush.
+        first = min((int(r["Dispatch_Id"]) for r in rows if "flush_kernel" in r["Kernel_Name"]), default=-1)
+        sk = [r for r in rows if _is_proj_kernel(r["Kernel_Name"]) and int(r["Dispatch_Id"]) > first]
         if len(sk) != len(seq):
             raise SystemExit("%s: %d projection launches, the pass makes %d" % (path, len(sk), len(seq)))
         return rows, sk
