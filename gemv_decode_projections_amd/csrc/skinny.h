@@ -172,6 +172,13 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
             for (int t = 0; t < NT; ++t)
                 xb[buf][u][t] = *reinterpret_cast<const u32x4 *>(xrow[t] + step * kStepK);
         }
+        // Keep a stage's loads where they are issued: the scheduler otherwise
+        // sinks them toward their first use, leaving 2-5 k-steps in flight
+        // per wave instead of 4-8 (cold sweeps: qkv_gate and the unpooler
+        // 0.3 us faster at 1-16 tokens, the pooler 1.2 us at 32). Waves that
+        // run a single stage (the router's) measured slower with it.
+        if constexpr (NSTAGE > 1 && !F32W)
+            __builtin_amdgcn_sched_barrier(0);
     };
 
     auto compute_stage = [&](int buf) {
