@@ -393,16 +393,18 @@ proj_config plan_default(int layer, int m, int zcr)
     // 1 GiB read before each call, so no weight byte is left in L2 or the
     // Infinity Cache), kept where they beat the next one by more than the
     // sweep's noise. The 12-bit form pays wherever the weight stream is long
-    // (qkv_gate, pooler, the full unpooler; up to 32 tokens, where 32-row
-    // workgroups read it once for one or two 16-token blocks); o's short
-    // stream does not hide the correction wave.
+    // (qkv_gate and pooler to 16 tokens, the full unpooler to 32); o's short
+    // stream does not hide the correction wave. At 17-32 tokens qkv_gate and
+    // the pooler read less per workgroup with 64-row tiles over both token
+    // blocks and a 4-way K split (each workgroup reads a quarter of x instead
+    // of all of it): in-process A/B 0.5 us faster at 32 tokens, 1.0-1.3 at 24.
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1}, {1, 2, 8, 16, 2, 1}, {1, 2, 8, 32, 1, 1}},
+        {{1, 1, 8, 32, 1, 1}, {1, 2, 8, 16, 2, 1}, {2, 4, 8, 8, 4, 0}},
         /* o         512 row blocks,  32 k-steps */
         {{1, 2, 8, 4, 1, 0}, {1, 2, 8, 4, 1, 0}, {2, 2, 4, 8, 1, 0}},
         /* pooler    256 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {1, 2, 8, 32, 1, 1}},
+        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {2, 4, 8, 8, 4, 0}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
         {{1, 1, 4, 8, 4, 0}, {1, 2, 8, 16, 1, 1}, {2, 2, 4, 32, 1, 1}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */

@@ -9,6 +9,7 @@ namespace gdp {
 const SkinnyVariant kSkinnyPartBf16Nt1[] = {
     GDP_WAVES_SPW(GDP_ENTRY, 1, 1, 0)
     GDP_WAVES_SPW(GDP_ENTRY, 1, 2, 0)
+    GDP_ENTRY(1, 4, 4, 8, 0) GDP_ENTRY(1, 4, 4, 16, 0) GDP_ENTRY(1, 4, 8, 8, 0) GDP_ENTRY(1, 4, 8, 16, 0)
 };
 const int kSkinnyPartBf16Nt1Count = sizeof(kSkinnyPartBf16Nt1) / sizeof(kSkinnyPartBf16Nt1[0]);
 

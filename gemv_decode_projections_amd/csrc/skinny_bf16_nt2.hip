@@ -9,6 +9,7 @@ namespace gdp {
 const SkinnyVariant kSkinnyPartBf16Nt2[] = {
     GDP_WAVES_SPW(GDP_ENTRY, 2, 1, 0)
     GDP_WAVES_SPW(GDP_ENTRY, 2, 2, 0)
+    GDP_ENTRY(2, 4, 4, 8, 0) GDP_ENTRY(2, 4, 4, 16, 0) GDP_ENTRY(2, 4, 8, 8, 0)
 };
 const int kSkinnyPartBf16Nt2Count = sizeof(kSkinnyPartBf16Nt2) / sizeof(kSkinnyPartBf16Nt2[0]);
 

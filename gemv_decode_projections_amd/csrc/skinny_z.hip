@@ -24,6 +24,7 @@ const SkinnyVariant kSkinnyPartZ[] = {
     GDP_Z_SET(2)
     GDP_Z_SET2(1)
     GDP_Z_SET2(2)
+    GDP_ENTRY(1, 4, 4, 8, 0) GDP_ENTRY(1, 4, 4, 16, 0) GDP_ENTRY(1, 4, 8, 8, 0) GDP_ENTRY(2, 4, 4, 8, 0)
 };
 const int kSkinnyPartZCount = sizeof(kSkinnyPartZ) / sizeof(kSkinnyPartZ[0]);
 
