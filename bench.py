@@ -327,9 +327,10 @@ def traffic_for(layer, m, kernel=None):
 def kernel_name(cfg, f32w):
     """Template name of the kernel a configuration launches (as profilers print it)."""
     f = "true" if f32w else "false"
-    if cfg.kind == 0:   # last argument: 12-bit weights
-        return "skinny_kernel<%d, %d, %d, %d, %s, %s>" % (cfg.nt, cfg.rb, cfg.waves, cfg.spw, f,
-                                                          "true" if cfg.flags & 4 else "false")
+    if cfg.kind == 0:   # last arguments: 12-bit weights, preloaded activation rows (0: none)
+        xp = 4 if cfg.flags & 32 else 8 if cfg.flags & 64 else 0
+        return "skinny_kernel<%d, %d, %d, %d, %s, %s, %d>" % (cfg.nt, cfg.rb, cfg.waves, cfg.spw, f,
+                                                              "true" if cfg.flags & 4 else "false", xp)
     if cfg.kind == 1:   # <rows per wave, token blocks, waves, k-steps per super-step, depth, fp32>
         return "tiled_kernel<%d, %d, %d, %d, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.waves,
                                                          min(4, cfg.spw // 2), cfg.spw, f)

@@ -67,6 +67,10 @@ constexpr int kMaxM = 1 << 30;
 // reduce drop their partials and the reducer polls once, so every reducer
 // gives up; a host-forced stand-in for a split that never arrives.
 constexpr int kFlagTestLostSplit = 16;
+// proj_config.flags bits 5 / 6 (skinny kernel, one 16-token block): each wave
+// loads its activation slice for at most 4 / 8 tokens into registers once.
+constexpr int kFlagPreload4 = 32;
+constexpr int kFlagPreload8 = 64;
 
 struct LayerState {
     void *wp = nullptr;
@@ -120,12 +124,13 @@ int skinny_part_count(int p)
     return counts[p];
 }
 
-const SkinnyVariant *find_variant(int nt, int rb, int waves, int spw, int f32w, int z)
+const SkinnyVariant *find_variant(int nt, int rb, int waves, int spw, int f32w, int z, int xp)
 {
     for (int p = 0; p < 4; ++p)
         for (int i = 0; i < skinny_part_count(p); ++i) {
             const SkinnyVariant &v = kSkinnyParts[p][i];
-            if (v.nt == nt && v.rb == rb && v.waves == waves && v.spw == spw && v.f32w == f32w && v.z == z)
+            if (v.nt == nt && v.rb == rb && v.waves == waves && v.spw == spw && v.f32w == f32w && v.z == z &&
+                v.xp == xp)
                 return &v;
         }
     return nullptr;
@@ -203,15 +208,21 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
     if (c.ksplit < 1)
         return PROJ_ERR_UNSUPPORTED;
     // Flag bits each kind understands: 0 placement (all), 2 12-bit weights
-    // (kind 0), 3 stream mode (kind 3), 4 the test-only lost split (kind 0).
-    const int known = 1 | (c.kind == 0 ? 4 | kFlagTestLostSplit : 0) | (c.kind == 3 ? 8 : 0);
+    // (kind 0), 3 stream mode (kind 3), 4 the test-only lost split (kind 0),
+    // 5 / 6 preloaded activations (kind 0).
+    const int known =
+        1 | (c.kind == 0 ? 4 | kFlagTestLostSplit | kFlagPreload4 | kFlagPreload8 : 0) | (c.kind == 3 ? 8 : 0);
     if (c.flags & ~known)
         return PROJ_ERR_UNSUPPORTED;
     if (c.kind == 0) {
         const int z = (c.flags & 4) ? 1 : 0;
         if (z && st.zcr < 0)
             return PROJ_ERR_UNSUPPORTED;              // no 12-bit form for this layer
-        const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w, z);
+        const int pre = c.flags & (kFlagPreload4 | kFlagPreload8);
+        const int xp = pre == kFlagPreload4 ? 4 : pre == kFlagPreload8 ? 8 : 0;
+        if (pre && (!xp || m > xp))
+            return PROJ_ERR_UNSUPPORTED;              // both bits, or more tokens than the preload holds
+        const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w, z, xp);
         if (!v)
             return PROJ_ERR_UNSUPPORTED;
         if (c.waves * c.spw * c.ksplit != KS)
@@ -387,6 +398,7 @@ proj_config plan_default(int layer, int m, int zcr)
 {
     struct Entry {
         int nt, rb, waves, spw, ksplit, z;   // z: read the 12-bit weights when the layer has them
+        int pre;                             // preload the activations (bucket 0 only)
     };
     // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32. Entries
     // are the fastest of every compiled configuration in cold sweeps (a plain
@@ -398,17 +410,21 @@ proj_config plan_default(int layer, int m, int zcr)
     // the pooler read less per workgroup with 64-row tiles over both token
     // blocks and a 4-way K split (each workgroup reads a quarter of x instead
     // of all of it): in-process A/B 0.5 us faster at 32 tokens, 1.0-1.3 at 24.
+    // Up to 8 tokens qkv_gate and the unpooler slice preload each wave's
+    // activations (flags bit 5 / 6): A/B 1.5 / 1.0 / 0.7 us faster on
+    // qkv_gate at 1 / 4 / 8 tokens, 0.1-0.2 on the slice; no gain on the
+    // pooler, which already runs at the plain read floor there.
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1}, {1, 2, 8, 16, 2, 1}, {2, 4, 8, 8, 4, 0}},
+        {{1, 1, 8, 32, 1, 1, 1}, {1, 2, 8, 16, 2, 1, 0}, {2, 4, 8, 8, 4, 0, 0}},
         /* o         512 row blocks,  32 k-steps */
-        {{1, 2, 8, 4, 1, 0}, {1, 2, 8, 4, 1, 0}, {2, 2, 4, 8, 1, 0}},
+        {{1, 2, 8, 4, 1, 0, 0}, {1, 2, 8, 4, 1, 0, 0}, {2, 2, 4, 8, 1, 0, 0}},
         /* pooler    256 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1}, {1, 1, 8, 32, 1, 1}, {2, 4, 8, 8, 4, 0}},
+        {{1, 1, 8, 32, 1, 1, 0}, {1, 1, 8, 32, 1, 1, 0}, {2, 4, 8, 8, 4, 0, 0}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
-        {{1, 1, 4, 8, 4, 0}, {1, 2, 8, 16, 1, 1}, {2, 2, 4, 32, 1, 1}},
+        {{1, 1, 4, 8, 4, 0, 1}, {1, 2, 8, 16, 1, 1, 0}, {2, 2, 4, 32, 1, 1, 0}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
-        {{1, 1, 8, 4, 8, 0}, {1, 1, 16, 2, 8, 0}, {1, 1, 16, 2, 8, 0}},
+        {{1, 1, 8, 4, 8, 0, 0}, {1, 1, 16, 2, 8, 0, 0}, {1, 1, 16, 2, 8, 0, 0}},
     };
     proj_config c{};
     // Few tokens on the router (m <= 8) and the unpooler slice (m <= 4):
@@ -433,6 +449,8 @@ proj_config plan_default(int layer, int m, int zcr)
         c.spw = e.spw;
         c.ksplit = e.ksplit;
         c.flags = (e.z && zcr >= 0) ? 4 : 0;
+        if (e.pre)
+            c.flags |= m <= 4 ? kFlagPreload4 : kFlagPreload8;
         return c;
     }
     // The router past 32 tokens stays on the skinny kernel: with 16 row
@@ -1057,7 +1075,7 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
         c.waves = v->waves;
         c.spw = v->spw;
         c.ksplit = 1;
-        c.flags = v->z ? 4 : 0;
+        c.flags = (v->z ? 4 : 0) | (v->xp == 4 ? kFlagPreload4 : v->xp == 8 ? kFlagPreload8 : 0);
         c.block = (v->waves + v->z) * kWave;
         *cfg = c;
     }

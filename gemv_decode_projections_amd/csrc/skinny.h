@@ -73,10 +73,17 @@ struct SkinnyArgs {
 
 constexpr int kZMaxSlots = 8;    // correction slots per row a 12-bit layer may use
 
-template <int NT, int RB, int WAVES, int SPW, bool F32W, bool Z = false>
+// XP > 0: at most XP (4 or 8) tokens; each wave loads its whole activation
+// slice (XP rows x SPW k-steps) into registers once instead of one 16-byte
+// load per lane and k-step, and takes every k-step's B fragment from those
+// registers with lane permutes. At <= 8 tokens a per-k-step load moves 1 KB
+// per wave for at most 8 rows x 64 useful bytes; dropping them measured
+// 0.7-2.1 us on the 8192-wide layers at one token.
+template <int NT, int RB, int WAVES, int SPW, bool F32W, bool Z = false, int XP = 0>
 __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(SkinnyArgs a)
 {
     static_assert(!(Z && F32W), "12-bit weights are BF16 only");
+    static_assert(XP == 0 || ((XP == 4 || XP == 8) && NT == 1 && !F32W), "preloaded activations: 4 or 8 rows, one token block");
     static_assert(!Z || WAVES > 1, "12-bit variants need a separate wave for the corrections");
     constexpr int U = SPW < 4 ? SPW : 4;             // k-steps per pipeline stage
     static_assert(SPW % U == 0, "SPW must be a multiple of the stage size");
@@ -136,6 +143,22 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     }
     const int perm_src = 4 * (lane % 16) + lane / 16;             // bpermute source lane
 
+    // Preloaded activations (XP > 0): register j of lane L holds the k-step
+    // the loop visits j * KPR + L / (4 XP)-th (the wave's run in its rotated
+    // order), token row (L % (4 XP)) / 4, k-group L % 4 (each lane quad one
+    // contiguous 64-byte row segment, as above). The B fragment of the s-th
+    // visited k-step (token l % 16, k-group l / 16) is then lane
+    // (s % KPR) * 4 XP + 4 (l % 16) + l / 16 of register s / KPR: one
+    // register index for the whole wave, known at compile time.
+    constexpr int KPR = XP ? 16 / XP : 1;                        // k-steps per register
+    constexpr int NXR = XP ? SPW / KPR : 1;                       // registers per lane
+    static_assert(XP == 0 || SPW % KPR == 0, "whole registers of k-steps");
+    u32x4 xp[NXR];
+    int xsrc[KPR];
+#pragma unroll
+    for (int q = 0; q < KPR; ++q)
+        xsrc[q] = (XP && lane % 16 < XP) ? q * 4 * XP + 4 * (lane % 16) + lane / 16 : 0;
+
     f32x4 acc[RB][NT];
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -168,9 +191,11 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
                         wa[buf][u][r][h] = f[h * kWave];
                 }
             }
+            if constexpr (XP == 0) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                xb[buf][u][t] = *reinterpret_cast<const u32x4 *>(xrow[t] + step * kStepK);
+                for (int t = 0; t < NT; ++t)
+                    xb[buf][u][t] = *reinterpret_cast<const u32x4 *>(xrow[t] + step * kStepK);
+            }
         }
         // Keep a stage's loads where they are issued: the scheduler otherwise
         // sinks them toward their first use, leaving 2-5 k-steps in flight
@@ -181,15 +206,22 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
             __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto compute_stage = [&](int buf) {
+    auto compute_stage = [&](int buf, int local) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 u32x4 v;
+                if constexpr (XP) {
+                    const int s = local + u;              // compile-time once the stages are unrolled
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_src * 4, (int)xb[buf][u][t][i]);
+                    for (int i = 0; i < 4; ++i)
+                        v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc[s % KPR] * 4, (int)xp[s / KPR][i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_src * 4, (int)xb[buf][u][t][i]);
+                }
                 xb[buf][u][t] = tok_ok[t] ? v : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
@@ -291,16 +323,25 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
           }
         }
     } else {
+        if constexpr (XP) {
+            const int row = (lane % (4 * XP)) / 4;
+            const int tok = tt * 16 + row;
+            const uint16_t *xr = a.x + (size_t)(tok < a.m ? tok : a.m - 1) * a.K + 8 * (lane % 4);
+#pragma unroll
+            for (int j = 0; j < NXR; ++j)
+                xp[j] = *reinterpret_cast<const u32x4 *>(
+                    xr + (size_t)(step0 + ((j * KPR + lane / (4 * XP) + rot) & (SPW - 1))) * kStepK);
+        }
         load_stage(0, 0);
         if constexpr (NSTAGE > 1)
             load_stage(1, U);
 #pragma unroll
         for (int s = 0; s < NSTAGE; s += 2) {
-            compute_stage(0);
+            compute_stage(0, s * U);
             if (s + 2 < NSTAGE)
                 load_stage(0, (s + 2) * U);
             if (s + 1 < NSTAGE) {
-                compute_stage(1);
+                compute_stage(1, (s + 1) * U);
                 if (s + 3 < NSTAGE)
                     load_stage(1, (s + 3) * U);
             }

@@ -25,6 +25,9 @@ const SkinnyVariant kSkinnyPartZ[] = {
     GDP_Z_SET2(1)
     GDP_Z_SET2(2)
     GDP_ENTRY(1, 4, 4, 8, 0) GDP_ENTRY(1, 4, 4, 16, 0) GDP_ENTRY(1, 4, 8, 8, 0) GDP_ENTRY(2, 4, 4, 8, 0)
+    // activations preloaded per wave (at most 4 / 8 tokens)
+    {1, 1, 8, 32, 0, reinterpret_cast<const void *>(&skinny_kernel<1, 1, 8, 32, false, true, 4>), 1, 4},
+    {1, 1, 8, 32, 0, reinterpret_cast<const void *>(&skinny_kernel<1, 1, 8, 32, false, true, 8>), 1, 8},
 };
 const int kSkinnyPartZCount = sizeof(kSkinnyPartZ) / sizeof(kSkinnyPartZ[0]);
 

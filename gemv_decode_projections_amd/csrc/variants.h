@@ -13,6 +13,7 @@ struct SkinnyVariant {
     int f32w;
     const void *fn;   // __global__ void (SkinnyArgs)
     int z;            // 1: reads the 12-bit weights (one extra wave per workgroup)
+    int xp;           // 4 or 8: activations preloaded per wave (at most that many tokens); 0: loaded per k-step
 };
 
 // Tiled (large-m) kernel variants: BMB x BNB blocks of 16 per workgroup, WR waves

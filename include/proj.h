@@ -229,6 +229,11 @@ int proj_last_hip_error(void);
  *             exit without publishing and the reducer polls once, so every
  *             reducer gives up (NaN outputs, counted by proj_split_giveups);
  *             a host-forced stand-in for a split that never arrives.
+ *             bit 5 / bit 6 set (kind 0, nt 1, m <= 4 / m <= 8; not both):
+ *             each wave loads its activation slice for 4 / 8 token rows into
+ *             registers once, instead of one load per k-step (compiled for
+ *             rb 1 with waves x spw 8 x 32 and 4 x 8). Same arithmetic and
+ *             summation order as with the bit clear.
  *             Other bits, or a bit the kind does not use, are rejected.
  * proj_plan fills the configuration proj_run would use; proj_run_config runs
  * an explicit one and returns PROJ_ERR_UNSUPPORTED if it is not compiled or
@@ -242,7 +247,8 @@ typedef struct {
     int spw;
     int ksplit;
     int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping); bit 2: 12-bit weights;
-                      bit 3: stream mode (kind 3) */
+                      bit 3: stream mode (kind 3); bit 4: test-only lost split (kind 0);
+                      bits 5 / 6: activations preloaded for <= 4 / <= 8 tokens (kind 0) */
     int grid;      /* filled by proj_plan: workgroups launched */
     int block;     /* filled by proj_plan: threads per workgroup */
 } proj_config;

@@ -92,6 +92,11 @@ def test_dispatch_plans_tile_every_layer(lib):
                 continue
             if cfg.kind == 0:
                 assert cfg.waves * cfg.spw * cfg.ksplit == k // 32
+                # preloaded activations: one 16-token block, at most 4 (bit 5) or 8 (bit 6) tokens
+                assert cfg.flags & 96 != 96
+                assert not cfg.flags & 32 or (m <= 4 and cfg.nt == 1)
+                assert not cfg.flags & 64 or (4 < m <= 8 and cfg.nt == 1)
+                assert bool(cfg.flags & 96) == (m <= 8 and name in ("qkv_gate", "unpooler"))
             elif cfg.kind == 1:
                 assert (k // 32) % (cfg.spw * cfg.ksplit) == 0
                 assert m > 32
@@ -116,7 +121,7 @@ def test_variant_registry(lib):
     seen = set()
     for i in range(nv):
         f32, cfg = binding.proj_variant(i)
-        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags & 4)
+        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags & (4 | 32 | 64))
         assert key not in seen
         seen.add(key)
     with pytest.raises(binding.ProjError):

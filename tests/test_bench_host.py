@@ -15,9 +15,9 @@ def _cfg(kind, nt, rb, waves, spw, ksplit=1, flags=0):
 
 
 def test_kernel_names_match_the_templates():
-    assert bench.kernel_name(_cfg(0, 1, 1, 8, 32), False) == "skinny_kernel<1, 1, 8, 32, false, false>"
-    assert bench.kernel_name(_cfg(0, 1, 1, 8, 32, flags=4), False) == "skinny_kernel<1, 1, 8, 32, false, true>"
-    assert bench.kernel_name(_cfg(0, 2, 1, 4, 16, 4), True) == "skinny_kernel<2, 1, 4, 16, true, false>"
+    assert bench.kernel_name(_cfg(0, 1, 1, 8, 32), False) == "skinny_kernel<1, 1, 8, 32, false, false, 0>"
+    assert bench.kernel_name(_cfg(0, 1, 1, 8, 32, flags=4), False) == "skinny_kernel<1, 1, 8, 32, false, true, 0>"
+    assert bench.kernel_name(_cfg(0, 2, 1, 4, 16, 4), True) == "skinny_kernel<2, 1, 4, 16, true, false, 0>"
     assert bench.kernel_name(_cfg(3, 4, 8, 4, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false, 4>"
     assert bench.kernel_name(_cfg(3, 4, 8, 4, 16, 2), False) == "wide_kernel<2, 4, 16, 4, false, false, 4>"
     assert bench.kernel_name(_cfg(3, 2, 4, 4, 8, 256, 8), True) == "wide_kernel<1, 2, 8, 2, true, true, 4>"
@@ -40,7 +40,7 @@ def _pmc_csv(path, counters, proj_value, copy_value=None, drop=0):
         for _ in range(5):       # prepare's warm-up launches, before the pass's first flush
             d += 1
             for c in counters:
-                w.writerow({"Dispatch_Id": d, "Kernel_Name": "void gdp::skinny_kernel<1, 1, 8, 32, false, true>(a)",
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": "void gdp::skinny_kernel<1, 1, 8, 32, false, true, 0>(a)",
                             "Grid_Size": 256, "Counter_Name": c, "Counter_Value": 1e9})
         for i, (name, layer) in enumerate(seq):
             d += 1
@@ -49,7 +49,7 @@ def _pmc_csv(path, counters, proj_value, copy_value=None, drop=0):
                             "Grid_Size": 1, "Counter_Name": c, "Counter_Value": 1})
             d += 1
             for c in counters:
-                w.writerow({"Dispatch_Id": d, "Kernel_Name": "void gdp::skinny_kernel<1, 1, 8, 32, false, false>(a)",
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": "void gdp::skinny_kernel<1, 1, 8, 32, false, false, 0>(a)",
                             "Grid_Size": 4096 + i, "Counter_Name": c, "Counter_Value": proj_value(name, layer, c)})
         for _ in range(3):
             d += 1
@@ -111,7 +111,7 @@ def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
         w.writeheader()
         t = 0
         for i in range(7):     # prepare's warm-up launches, before any flush
-            w.writerow({"Kernel_Name": "void gdp::skinny_kernel<1, 1, 8, 32, false, true>(a)", "Start_Timestamp": t,
+            w.writerow({"Kernel_Name": "void gdp::skinny_kernel<1, 1, 8, 32, false, true, 0>(a)", "Start_Timestamp": t,
                         "End_Timestamp": t + 5000, "Grid_Size_X": 256})
             t += 6000
         for i, (tag, layer, m) in enumerate(seq):
@@ -155,7 +155,7 @@ def _graph_trace(path, reps, gap_ns=700):
                 add("gdp::(anonymous namespace)::flush_kernel<false>(a)", 200000)
                 add("gdp::(anonymous namespace)::stamp_kernel(a, b)", 1000)
                 for i, layer in enumerate(LAYERS):
-                    k = ("void gdp::skinny_kernel<1, 1, 8, 32, false, false>(a)" if which == "load"
+                    k = ("void gdp::skinny_kernel<1, 1, 8, 32, false, false, 0>(a)" if which == "load"
                          else "gdp::(anonymous namespace)::read_floor_kernel<4, false>(a)")
                     add(k, 1000 * (i + 1) + (100 * j if which == "load" else 0))
                 add("gdp::(anonymous namespace)::stamp_kernel(a, b)", 1000)

@@ -152,7 +152,9 @@ def _variant_cases():
 def test_every_compiled_variant(case):
     layer, kind, nt, rb, waves, spw, split, flags = case
     p = prepared(0)
-    if kind == 0:
+    if kind == 0 and flags & (32 | 64):
+        ms = [1, 3, 4] if flags & 32 else [1, 5, 8]     # preloaded activations: at most 4 / 8 tokens
+    elif kind == 0:
         ms = [1, 16 * nt - 3, 16 * nt + 5]
     elif kind in (1, 3):
         ms = [33, 16 * nt + 5, 3 * 16 * nt - 7]
@@ -213,6 +215,34 @@ def test_wide_stream_mode_rejects_more_workgroups_than_super_steps():
                 binding.ProjConfig.make(kind=1, nt=2, rb=4, waves=4, spw=8, ksplit=1, flags=8)):
         with pytest.raises(binding.ProjError):
             binding.proj_run_config("o", x, m, out, bad)
+
+
+def test_preload_flags_checked_against_token_count():
+    """Preloaded activations hold 4 (bit 5) or 8 (bit 6) token rows of one
+    16-token block: more tokens, both bits or two token blocks are rejected
+    before launch; within the limit the output matches the per-k-step form
+    bit for bit (same arithmetic, same summation order)."""
+    p = prepared(0)
+    mk = binding.ProjConfig.make
+    for m in (4, 5, 8, 9):
+        xs = make_x("qkv_gate", m, seed=2100 + m, outliers=True)
+        x = to_device_x(xs.bits)
+        out = binding.new_out("qkv_gate", m)
+        base = run_layer("qkv_gate", xs.bits, cfg=mk(kind=0, nt=1, rb=1, waves=8, spw=32, ksplit=1, flags=4))
+        for flags, fits in ((4 | 32, m <= 4), (4 | 64, m <= 8), (4 | 96, False)):
+            cfg = mk(kind=0, nt=1, rb=1, waves=8, spw=32, ksplit=1, flags=flags)
+            if not fits:
+                with pytest.raises(binding.ProjError):
+                    binding.proj_run_config("qkv_gate", x, m, out, cfg)
+                continue
+            say("preload", "qkv_gate", "m=%d flags=%d" % (m, flags))
+            got = run_layer("qkv_gate", xs.bits, cfg=cfg)
+            assert np.array_equal(got, base), (m, flags)
+            assert compare("qkv_gate", got, p.w["qkv_gate"], xs).ok
+    with pytest.raises(binding.ProjError):
+        binding.proj_run_config("qkv_gate", to_device_x(make_x("qkv_gate", 4, seed=1).bits), 4,
+                                binding.new_out("qkv_gate", 4),
+                                mk(kind=0, nt=2, rb=1, waves=8, spw=32, ksplit=1, flags=64))
 
 
 @pytest.mark.parametrize("layer,m", [("router", 1), ("router", 32), ("unpooler", 8)])
