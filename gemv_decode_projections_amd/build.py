@@ -26,6 +26,7 @@ SOURCES = [
     "tiled_variants.hip",
     "rowdot_variants.hip",
     "wide_variants.hip",
+    "wide_dma_variants.hip",
 ]
 
 ARCH = os.environ.get("GDP_OFFLOAD_ARCH", "gfx950")
@@ -47,6 +48,7 @@ COMMON = [
 EXTRA = {
     "tiled_variants.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "wide_variants.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "wide_dma_variants.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

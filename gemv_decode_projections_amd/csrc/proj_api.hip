@@ -71,6 +71,8 @@ constexpr int kFlagTestLostSplit = 16;
 // loads its activation slice for at most 4 / 8 tokens into registers once.
 constexpr int kFlagPreload4 = 32;
 constexpr int kFlagPreload8 = 64;
+// proj_config.flags bit 7 (wide-tile kernel): activations by LDS DMA.
+constexpr int kFlagDma = 128;
 
 struct LayerState {
     void *wp = nullptr;
@@ -146,11 +148,19 @@ const TiledVariant *find_tiled(int bmb, int bnb, int waves, int depth, int f32w)
     return nullptr;
 }
 
-const WideVariant *find_wide(int bmb, int bnb, int depth, int f32w, int waves)
+int wide_variant_count() { return kWideVariantCount + kWideDmaVariantCount; }
+
+const WideVariant &wide_variant_at(int i)
 {
-    for (int i = 0; i < kWideVariantCount; ++i) {
-        const WideVariant &v = kWideVariants[i];
-        if (v.bmb == bmb && v.bnb == bnb && v.depth == depth && v.f32w == f32w && v.waves == waves)
+    return i < kWideVariantCount ? kWideVariants[i] : kWideDmaVariants[i - kWideVariantCount];
+}
+
+const WideVariant *find_wide(int bmb, int bnb, int depth, int f32w, int waves, int xdma)
+{
+    for (int i = 0; i < wide_variant_count(); ++i) {
+        const WideVariant &v = wide_variant_at(i);
+        if (v.bmb == bmb && v.bnb == bnb && v.depth == depth && v.f32w == f32w && v.waves == waves &&
+            v.xdma == xdma)
             return &v;
     }
     return nullptr;
@@ -171,7 +181,7 @@ int skinny_variants()
     return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count + kSkinnyPartZCount;
 }
 
-int total_variants() { return skinny_variants() + kTiledVariantCount + kRowVariantCount + kWideVariantCount; }
+int total_variants() { return skinny_variants() + kTiledVariantCount + kRowVariantCount + wide_variant_count(); }
 
 const SkinnyVariant *variant_at(int i)
 {
@@ -209,9 +219,9 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
         return PROJ_ERR_UNSUPPORTED;
     // Flag bits each kind understands: 0 placement (all), 2 12-bit weights
     // (kind 0), 3 stream mode (kind 3), 4 the test-only lost split (kind 0),
-    // 5 / 6 preloaded activations (kind 0).
-    const int known =
-        1 | (c.kind == 0 ? 4 | kFlagTestLostSplit | kFlagPreload4 | kFlagPreload8 : 0) | (c.kind == 3 ? 8 : 0);
+    // 5 / 6 preloaded activations (kind 0), 7 activations by LDS DMA (kind 3).
+    const int known = 1 | (c.kind == 0 ? 4 | kFlagTestLostSplit | kFlagPreload4 | kFlagPreload8 : 0) |
+                      (c.kind == 3 ? 8 | kFlagDma : 0);
     if (c.flags & ~known)
         return PROJ_ERR_UNSUPPORTED;
     if (c.kind == 0) {
@@ -309,7 +319,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
         // spw = weight prefetch depth in k-steps; K split unevenly in
         // super-steps of 2 (4 at depth 16) k-steps. flags bit 3: stream mode,
         // ksplit = number of workgroups sharing all tiles' super-steps.
-        const WideVariant *v = find_wide(c.rb, c.nt, c.spw, f32w, c.waves);
+        const WideVariant *v = find_wide(c.rb, c.nt, c.spw, f32w, c.waves, (c.flags & kFlagDma) ? 1 : 0);
         if (!v)
             return PROJ_ERR_UNSUPPORTED;
         if (ne % (kRowsPerBlock * c.rb) != 0 || c.ksplit < 1)
@@ -502,16 +512,22 @@ proj_config plan_default(int layer, int m, int zcr)
     // grid within one workgroup per compute unit (a grid past 256 measured
     // far slower: qkv_gate m = 130 with 64-token tiles took 18.7 us at 4
     // splits, 216 workgroups, 32.4 at 5, 270 workgroups, and 24.5 at 3).
+    // dma: the wide-tile kernel moves activations by LDS DMA (flags bit 7).
+    // In-process cold A/B against register staging (us): pooler m = 128 /
+    // 256 / 512 / 1000 24.8 / 32.9 / 53.9 / 88.9 -> 24.3 / 31.6 / 52.5 / 85.3;
+    // unpooler m = 256 / 512 / 1000 30.7 / 47.7 / 62.5 -> 30.0 / 47.0 / 60.3;
+    // qkv_gate m = 256 25.7 -> 25.1. Elsewhere it tied or lost (o m = 256
+    // 11.3 -> 12.3, qkv_gate m = 128 19.0 -> 19.5).
     struct TEntry {
-        int kind, rb, nt, waves, depth, ksplit;
+        int kind, rb, nt, waves, depth, ksplit, dma;
     };
     // Measured in the same cold sweeps (m = 64, 128, 256); bucket 3 (past 256
     // tokens) keeps its split rule below.
     static const TEntry ttable[PROJ_ROUTER][4] = {   // the four BF16 layers
-        /* qkv_gate */ {{3, 4, 4, 4, 16, 6}, {3, 4, 4, 4, 16, 3}, {3, 8, 4, 4, 16, 0}, {3, 8, 4, 4, 16, 0}},
-        /* o        */ {{1, 4, 2, 4, 16, 1}, {1, 8, 2, 4, 8, 1}, {3, 8, 4, 4, 4, 0}, {3, 8, 4, 4, 4, 0}},
-        /* pooler   */ {{3, 4, 4, 4, 8, 4}, {3, 8, 4, 4, 8, 4}, {3, 8, 8, 8, 8, 0}, {3, 8, 4, 4, 16, 0}},
-        /* unpooler */ {{1, 4, 2, 4, 16, 1}, {3, 4, 4, 4, 16, 1}, {3, 8, 4, 4, 16, 0}, {3, 8, 4, 4, 16, 0}},
+        /* qkv_gate */ {{3, 4, 4, 4, 16, 6, 0}, {3, 4, 4, 4, 16, 3, 0}, {3, 8, 4, 4, 16, 0, 1}, {3, 8, 4, 4, 16, 0, 0}},
+        /* o        */ {{1, 4, 2, 4, 16, 1, 0}, {1, 8, 2, 4, 8, 1, 0}, {3, 8, 4, 4, 4, 0, 0}, {3, 8, 4, 4, 4, 0, 0}},
+        /* pooler   */ {{3, 4, 4, 4, 8, 4, 0}, {3, 8, 4, 4, 8, 4, 1}, {3, 8, 8, 8, 8, 0, 1}, {3, 8, 4, 4, 16, 0, 1}},
+        /* unpooler */ {{1, 4, 2, 4, 16, 1, 0}, {3, 4, 4, 4, 16, 1, 0}, {3, 8, 4, 4, 16, 0, 1}, {3, 8, 4, 4, 16, 0, 1}},
     };
     const int ne = n_eff_of(layer, m);
     // Past 256 tokens the 8-wave wide kernel (two waves per SIMD) holds
@@ -535,6 +551,7 @@ proj_config plan_default(int layer, int m, int zcr)
         c.waves = 8;
         c.spw = 8;
         c.ksplit = 5;
+        c.flags = ttable[layer][2].dma ? kFlagDma : 0;
         return c;
     }
     if (m > 256 && ne % 256 == 0) {
@@ -560,6 +577,7 @@ proj_config plan_default(int layer, int m, int zcr)
             while (ks > 1 && tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes)
                 --ks;
             c.ksplit = ks;
+            c.flags = ttable[layer][3].dma ? kFlagDma : 0;
             return c;
         }
     }
@@ -579,6 +597,7 @@ proj_config plan_default(int layer, int m, int zcr)
     while (ks > 1 && (tiles * ks > 768 || tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes))
         ks = e.kind == 3 ? ks - 1 : ks / 2;   // the tiled kernel splits K into equal powers of two
     c.ksplit = ks;
+    c.flags = (e.kind == 3 && e.dma) ? kFlagDma : 0;
     return c;
 }
 
@@ -1012,7 +1031,7 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
 {
     const int wide0 = skinny_variants() + kTiledVariantCount + kRowVariantCount;
     if (i >= wide0 && i < total_variants()) {
-        const WideVariant &w = kWideVariants[i - wide0];
+        const WideVariant &w = wide_variant_at(i - wide0);
         if (is_f32w)
             *is_f32w = w.f32w;
         if (cfg) {
@@ -1024,6 +1043,7 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
             c.spw = w.depth;
             c.ksplit = 1;
             c.block = w.waves * kWave;
+            c.flags = w.xdma ? kFlagDma : 0;
             *cfg = c;
         }
         return PROJ_OK;

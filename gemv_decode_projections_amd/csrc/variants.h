@@ -47,6 +47,7 @@ struct WideVariant {
     int waves;        // 4 or 8
     const void *fn;          // __global__ void (WideArgs): one tile per workgroup
     const void *fn_stream;   // the same kernel in stream mode
+    int xdma;                // 1: activations by LDS DMA (wide_kernel's XDMA)
 };
 
 // Each part is defined in its own translation unit so the variants compile in parallel.
@@ -62,6 +63,8 @@ extern const TiledVariant kTiledVariants[];
 extern const int kTiledVariantCount;
 extern const WideVariant kWideVariants[];
 extern const int kWideVariantCount;
+extern const WideVariant kWideDmaVariants[];
+extern const int kWideDmaVariantCount;
 extern const RowVariant kRowVariants[];
 extern const int kRowVariantCount;
 

@@ -234,6 +234,9 @@ int proj_last_hip_error(void);
  *             registers once, instead of one load per k-step (compiled for
  *             rb 1 with waves x spw 8 x 32 and 4 x 8). Same arithmetic and
  *             summation order as with the bit clear.
+ *             bit 7 set (kind 3, BF16 weights): activations move from memory
+ *             straight into the LDS ring by DMA instead of through registers;
+ *             same arithmetic and summation order as with the bit clear.
  *             Other bits, or a bit the kind does not use, are rejected.
  * proj_plan fills the configuration proj_run would use; proj_run_config runs
  * an explicit one and returns PROJ_ERR_UNSUPPORTED if it is not compiled or
@@ -248,7 +251,8 @@ typedef struct {
     int ksplit;
     int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping); bit 2: 12-bit weights;
                       bit 3: stream mode (kind 3); bit 4: test-only lost split (kind 0);
-                      bits 5 / 6: activations preloaded for <= 4 / <= 8 tokens (kind 0) */
+                      bits 5 / 6: activations preloaded for <= 4 / <= 8 tokens (kind 0);
+                      bit 7: activations by LDS DMA (kind 3) */
     int grid;      /* filled by proj_plan: workgroups launched */
     int block;     /* filled by proj_plan: threads per workgroup */
 } proj_config;

@@ -110,6 +110,10 @@ def test_dispatch_plans_tile_every_layer(lib):
                                                              name == "pooler" and 128 < m <= 192 and cfg.nt == 4)) \
                     or (name == "pooler" and 64 < m <= 256 and cfg.rb == 8)
                 assert 1 <= cfg.ksplit <= k // (128 if cfg.spw >= 16 else 64)
+                # activations by LDS DMA (bit 7) where it measured faster; no other bit
+                dma = (name == "pooler" and m > 64) or (name == "unpooler" and m > 128) or \
+                      (name == "qkv_gate" and 128 < m <= 256)
+                assert cfg.flags == (128 if dma else 0)
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
             assert cfg.grid == ne // (16 * cfg.rb) * n_tt * cfg.ksplit
@@ -121,7 +125,7 @@ def test_variant_registry(lib):
     seen = set()
     for i in range(nv):
         f32, cfg = binding.proj_variant(i)
-        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags & (4 | 32 | 64))
+        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags & (4 | 32 | 64 | 128))
         assert key not in seen
         seen.add(key)
     with pytest.raises(binding.ProjError):

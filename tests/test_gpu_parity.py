@@ -141,9 +141,10 @@ def _variant_cases():
                 cases.append((layer, 1, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 2, 1))  # split groups across XCDs
                 break
             elif cfg.kind == 3 and n % (16 * cfg.rb) == 0:
-                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 1, 0))
-                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 3, 0))   # uneven split lengths
-                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 5, 1))   # uneven, across XCDs
+                f = cfg.flags                                                            # bit 7: LDS DMA
+                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 1, f))
+                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 3, f))   # uneven split lengths
+                cases.append((layer, 3, cfg.nt, cfg.rb, cfg.waves, cfg.spw, 5, f | 1))   # uneven, across XCDs
                 break
     return cases
 
@@ -182,7 +183,10 @@ def test_every_compiled_variant(case):
 # FP32 weights.
 _STREAM_CASES = [("qkv_gate", 256, 8, 4, 8, 256, 8), ("qkv_gate", 130, 4, 4, 8, 250, 9),
                  ("pooler", 200, 8, 4, 16, 256, 8), ("o", 33, 8, 4, 4, 1024, 8), ("o", 33, 8, 4, 8, 1, 8),
-                 ("unpooler", 400, 8, 8, 8, 264, 8), ("router", 256, 4, 2, 8, 256, 8)]
+                 ("unpooler", 400, 8, 8, 8, 264, 8), ("router", 256, 4, 2, 8, 256, 8),
+                 # activations by LDS DMA (bit 7): several segments per workgroup refill the ring
+                 ("qkv_gate", 130, 4, 4, 8, 250, 137), ("pooler", 200, 8, 4, 16, 256, 136),
+                 ("o", 33, 8, 4, 8, 1, 136)]
 
 
 @pytest.mark.parametrize("case", _STREAM_CASES, ids=lambda c: "%s-m%d-rb%d-nt%d-d%d-g%d-f%d" % c)
@@ -202,6 +206,30 @@ def test_wide_stream_mode(case):
     assert np.array_equal(got, again)
 
 
+@pytest.mark.parametrize("layer,m", [("qkv_gate", 33), ("qkv_gate", 256), ("o", 256), ("pooler", 130),
+                                     ("pooler", 256), ("unpooler", 128), ("unpooler", 300), ("pooler", 1000)])
+def test_wide_dma_matches_register_staging(layer, m):
+    """The wide-tile plan with its activations moved by LDS DMA (flags bit 7)
+    gives the same bits as with them staged through registers: the same
+    products summed in the same order."""
+    p = prepared(0)
+    cfg = binding.proj_plan(layer, m)
+    if cfg.kind != 3:
+        pytest.skip("plan is not the wide-tile kernel")
+    xs = make_x(layer, m, seed=2200 + m, outliers=True)
+    base = run_layer(layer, xs.bits, cfg=cfg)
+    dma = binding.ProjConfig.make(kind=3, nt=cfg.nt, rb=cfg.rb, waves=cfg.waves, spw=cfg.spw,
+                                  ksplit=cfg.ksplit, flags=(cfg.flags & ~128) | 128)
+    say("dma", layer, "m=%d" % m, dma.as_dict())
+    got = run_layer(layer, xs.bits, cfg=dma)
+    assert np.array_equal(got, base)
+    nodma = binding.ProjConfig.make(kind=3, nt=cfg.nt, rb=cfg.rb, waves=cfg.waves, spw=cfg.spw,
+                                    ksplit=cfg.ksplit, flags=cfg.flags & ~128)
+    assert np.array_equal(run_layer(layer, xs.bits, cfg=nodma), base)
+    rows = sample_rows(xs, m) if m >= 100 else None
+    assert compare(layer, got, p.w[layer], xs, rows=rows).ok
+
+
 def test_wide_stream_mode_rejects_more_workgroups_than_super_steps():
     prepared(0)
     m, n_rt, nss = 33, 8192 // 128, 1024 // 32 // 2        # layer o, 128-row tiles, one token tile
@@ -212,6 +240,7 @@ def test_wide_stream_mode_rejects_more_workgroups_than_super_steps():
     torch.cuda.synchronize()
     for bad in (binding.ProjConfig.make(kind=3, nt=4, rb=8, waves=4, spw=8, ksplit=n_rt * nss + 1, flags=8),
                 binding.ProjConfig.make(kind=3, nt=4, rb=8, waves=4, spw=8, ksplit=2, flags=16),
+                binding.ProjConfig.make(kind=3, nt=4, rb=8, waves=4, spw=8, ksplit=2, flags=32),
                 binding.ProjConfig.make(kind=1, nt=2, rb=4, waves=4, spw=8, ksplit=1, flags=8)):
         with pytest.raises(binding.ProjError):
             binding.proj_run_config("o", x, m, out, bad)
@@ -432,6 +461,25 @@ def test_split_giveup_is_counted_and_cleaned(layer, m):
         assert r.ok, (c.as_dict(), r)
     assert binding.proj_split_giveups(layer, reset=True) == n_tiles * 3
     assert binding.proj_split_giveups(layer) == 0
+
+
+def test_no_split_giveups_in_normal_use():
+    """No polled split-K reducer gives up in normal use: not in prepare's
+    warm-up launches and not over every load's plans (a give-up there would
+    mean a reducer stopped waiting for a partial that was on its way, whose
+    late words would then read as arrived in a later launch)."""
+    prepared(0)
+    for layer in SHAPES:
+        assert binding.proj_split_giveups(layer) == 0, layer
+    for m in LOADS.values():
+        for layer in SHAPES:
+            xs = make_x(layer, m, seed=2300 + m)
+            run_layer(layer, xs.bits)
+    for m in (33, 64, 130, 300, 512, 1000):
+        for layer in SHAPES:
+            run_layer(layer, make_x(layer, m, seed=2400 + m).bits)
+    for layer in SHAPES:
+        assert binding.proj_split_giveups(layer) == 0, layer
 
 
 def _exception_columns(w, limit=3):
