@@ -334,10 +334,11 @@ def kernel_name(cfg, f32w):
     if cfg.kind == 1:   # <rows per wave, token blocks, waves, k-steps per super-step, depth, fp32>
         return "tiled_kernel<%d, %d, %d, %d, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.waves,
                                                          min(4, cfg.spw // 2), cfg.spw, f)
-    if cfg.kind == 3:   # <rows per wave, token blocks, depth, k-steps per super-step, fp32, stream, waves>
-        return "wide_kernel<%d, %d, %d, %d, %s, %s, %d>" % (cfg.rb // cfg.waves, cfg.nt, cfg.spw,
-                                                           4 if cfg.spw >= 16 else 2, f,
-                                                           "true" if cfg.flags & 8 else "false", cfg.waves)
+    if cfg.kind == 3:   # <rows per wave, token blocks, depth, k-steps per super-step, fp32, stream, waves, LDS DMA>
+        return "wide_kernel<%d, %d, %d, %d, %s, %s, %d, %s>" % (cfg.rb // cfg.waves, cfg.nt, cfg.spw,
+                                                               4 if cfg.spw >= 16 else 2, f,
+                                                               "true" if cfg.flags & 8 else "false", cfg.waves,
+                                                               "true" if cfg.flags & 128 else "false")
     return "rowdot_kernel<%d, %d, %d, %s>" % (cfg.nt, cfg.rb, cfg.spw, f)
 
 

@@ -423,16 +423,20 @@ proj_config plan_default(int layer, int m, int zcr)
     // Up to 8 tokens qkv_gate and the unpooler slice preload each wave's
     // activations (flags bit 5 / 6): A/B 1.5 / 1.0 / 0.7 us faster on
     // qkv_gate at 1 / 4 / 8 tokens, 0.1-0.2 on the slice; no gain on the
-    // pooler, which already runs at the plain read floor there.
+    // pooler, which already runs at the plain read floor there. At 9-16
+    // tokens qkv_gate takes 4-wave workgroups of 16 k-steps per wave with a
+    // 4-way split and the unpooler 4-wave workgroups of two row blocks over
+    // the whole K (in-process A/B at m = 9 / 12 / 16: qkv_gate 0.32 / 0.36 /
+    // 0.16 us faster, unpooler 0.24 / 0.28 / 0.20).
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1, 1}, {1, 2, 8, 16, 2, 1, 0}, {2, 4, 8, 8, 4, 0, 0}},
+        {{1, 1, 8, 32, 1, 1, 1}, {1, 1, 4, 16, 4, 1, 0}, {2, 4, 8, 8, 4, 0, 0}},
         /* o         512 row blocks,  32 k-steps */
         {{1, 2, 8, 4, 1, 0, 0}, {1, 2, 8, 4, 1, 0, 0}, {2, 2, 4, 8, 1, 0, 0}},
         /* pooler    256 row blocks, 256 k-steps */
         {{1, 1, 8, 32, 1, 1, 0}, {1, 1, 8, 32, 1, 1, 0}, {2, 4, 8, 8, 4, 0, 0}},
         /* unpooler  64 (slice) / 512 row blocks, 128 k-steps */
-        {{1, 1, 4, 8, 4, 0, 1}, {1, 2, 8, 16, 1, 1, 0}, {2, 2, 4, 32, 1, 1, 0}},
+        {{1, 1, 4, 8, 4, 0, 1}, {1, 2, 4, 32, 1, 1, 0}, {2, 2, 4, 32, 1, 1, 0}},
         /* router    16 row blocks, 256 k-steps of FP32 weights */
         {{1, 1, 8, 4, 8, 0, 0}, {1, 1, 16, 2, 8, 0, 0}, {1, 1, 16, 2, 8, 0, 0}},
     };

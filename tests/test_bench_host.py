@@ -18,10 +18,11 @@ def test_kernel_names_match_the_templates():
     assert bench.kernel_name(_cfg(0, 1, 1, 8, 32), False) == "skinny_kernel<1, 1, 8, 32, false, false, 0>"
     assert bench.kernel_name(_cfg(0, 1, 1, 8, 32, flags=4), False) == "skinny_kernel<1, 1, 8, 32, false, true, 0>"
     assert bench.kernel_name(_cfg(0, 2, 1, 4, 16, 4), True) == "skinny_kernel<2, 1, 4, 16, true, false, 0>"
-    assert bench.kernel_name(_cfg(3, 4, 8, 4, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false, 4>"
-    assert bench.kernel_name(_cfg(3, 4, 8, 4, 16, 2), False) == "wide_kernel<2, 4, 16, 4, false, false, 4>"
-    assert bench.kernel_name(_cfg(3, 2, 4, 4, 8, 256, 8), True) == "wide_kernel<1, 2, 8, 2, true, true, 4>"
-    assert bench.kernel_name(_cfg(3, 4, 16, 8, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false, 8>"
+    assert bench.kernel_name(_cfg(3, 4, 8, 4, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false, 4, false>"
+    assert bench.kernel_name(_cfg(3, 4, 8, 4, 16, 2), False) == "wide_kernel<2, 4, 16, 4, false, false, 4, false>"
+    assert bench.kernel_name(_cfg(3, 2, 4, 4, 8, 256, 8), True) == "wide_kernel<1, 2, 8, 2, true, true, 4, false>"
+    assert bench.kernel_name(_cfg(3, 4, 16, 8, 8, 2), False) == "wide_kernel<2, 4, 8, 2, false, false, 8, false>"
+    assert bench.kernel_name(_cfg(3, 8, 8, 8, 8, 4, 128), False) == "wide_kernel<1, 8, 8, 2, false, false, 8, true>"
     assert bench.kernel_name(_cfg(1, 2, 8, 4, 8), False) == "tiled_kernel<2, 2, 4, 4, 8, false>"
     assert bench.kernel_name(_cfg(2, 8, 1, 4, 4), True) == "rowdot_kernel<8, 1, 4, true>"
 
@@ -119,7 +120,7 @@ def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
                         "End_Timestamp": t + 100000, "Grid_Size_X": 1})
             t += 100000
             dur = 1000 * (LAYERS.index(layer) + 1) + m + (500 if tag.startswith("warmup") else 0)   # ns
-            w.writerow({"Kernel_Name": "void gdp::wide_kernel<2, 4, 8, 2, false, false, 4>(a)",
+            w.writerow({"Kernel_Name": "void gdp::wide_kernel<2, 4, 8, 2, false, false, 4, false>(a)",
                         "Start_Timestamp": t, "End_Timestamp": t + dur, "Grid_Size_X": 256})
             t += dur
     r = bench.summarize_loads_trace(str(path), *counts)
@@ -130,7 +131,7 @@ def test_loads_trace_summary_matches_the_launch_sequence(tmp_path):
         for layer in LAYERS:
             assert lay[layer]["n"] == counts[0]
             assert lay[layer]["median_us"] == pytest.approx((1000 * (LAYERS.index(layer) + 1) + m) / 1e3)
-            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false, 4>"
+            assert lay[layer]["kernel"] == "wide_kernel<2, 4, 8, 2, false, false, 4, false>"
         assert r["graph:" + name]["layers"]["o"]["n"] == counts[4]
     for m in AWKWARD_M:
         assert r["m=%d" % m]["m"] == m
