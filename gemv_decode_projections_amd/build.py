@@ -23,6 +23,7 @@ SOURCES = [
     "skinny_bf16_nt2.hip",
     "skinny_f32.hip",
     "skinny_z.hip",
+    "skinny_sk.hip",
     "tiled_variants.hip",
     "rowdot_variants.hip",
     "wide_variants.hip",

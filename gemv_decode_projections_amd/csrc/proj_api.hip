@@ -73,6 +73,9 @@ constexpr int kFlagPreload4 = 32;
 constexpr int kFlagPreload8 = 64;
 // proj_config.flags bit 7 (wide-tile kernel): activations by LDS DMA.
 constexpr int kFlagDma = 128;
+// proj_config.flags bit 8 (skinny kernel, rb 1, one token block): the stream
+// partition of the (row block, k-step) units over the workgroups.
+constexpr int kFlagStream = 256;
 
 struct LayerState {
     void *wp = nullptr;
@@ -117,22 +120,24 @@ int n_eff_of(int layer, int m)
     return kLayers[layer].N;
 }
 
-const SkinnyVariant *const kSkinnyParts[4] = {kSkinnyPartBf16Nt1, kSkinnyPartBf16Nt2, kSkinnyPartF32, kSkinnyPartZ};
+constexpr int kSkinnyPartCount = 5;
+const SkinnyVariant *const kSkinnyParts[kSkinnyPartCount] = {kSkinnyPartBf16Nt1, kSkinnyPartBf16Nt2, kSkinnyPartF32,
+                                                             kSkinnyPartZ, kSkinnyPartStream};
 
 int skinny_part_count(int p)
 {
-    const int counts[4] = {kSkinnyPartBf16Nt1Count, kSkinnyPartBf16Nt2Count, kSkinnyPartF32Count,
-                           kSkinnyPartZCount};
+    const int counts[kSkinnyPartCount] = {kSkinnyPartBf16Nt1Count, kSkinnyPartBf16Nt2Count, kSkinnyPartF32Count,
+                                          kSkinnyPartZCount, kSkinnyPartStreamCount};
     return counts[p];
 }
 
-const SkinnyVariant *find_variant(int nt, int rb, int waves, int spw, int f32w, int z, int xp)
+const SkinnyVariant *find_variant(int nt, int rb, int waves, int spw, int f32w, int z, int xp, int skm)
 {
-    for (int p = 0; p < 4; ++p)
+    for (int p = 0; p < kSkinnyPartCount; ++p)
         for (int i = 0; i < skinny_part_count(p); ++i) {
             const SkinnyVariant &v = kSkinnyParts[p][i];
             if (v.nt == nt && v.rb == rb && v.waves == waves && v.spw == spw && v.f32w == f32w && v.z == z &&
-                v.xp == xp)
+                v.xp == xp && v.skm == skm)
                 return &v;
         }
     return nullptr;
@@ -178,7 +183,10 @@ const RowVariant *find_row(int mcap, int r, int kit, int f32w)
 
 int skinny_variants()
 {
-    return kSkinnyPartBf16Nt1Count + kSkinnyPartBf16Nt2Count + kSkinnyPartF32Count + kSkinnyPartZCount;
+    int n = 0;
+    for (int p = 0; p < kSkinnyPartCount; ++p)
+        n += skinny_part_count(p);
+    return n;
 }
 
 int total_variants() { return skinny_variants() + kTiledVariantCount + kRowVariantCount + wide_variant_count(); }
@@ -187,7 +195,7 @@ const SkinnyVariant *variant_at(int i)
 {
     if (i < 0)
         return nullptr;
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < kSkinnyPartCount; ++p) {
         if (i < skinny_part_count(p))
             return &kSkinnyParts[p][i];
         i -= skinny_part_count(p);
@@ -220,7 +228,7 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
     // Flag bits each kind understands: 0 placement (all), 2 12-bit weights
     // (kind 0), 3 stream mode (kind 3), 4 the test-only lost split (kind 0),
     // 5 / 6 preloaded activations (kind 0), 7 activations by LDS DMA (kind 3).
-    const int known = 1 | (c.kind == 0 ? 4 | kFlagTestLostSplit | kFlagPreload4 | kFlagPreload8 : 0) |
+    const int known = 1 | (c.kind == 0 ? 4 | kFlagTestLostSplit | kFlagPreload4 | kFlagPreload8 | kFlagStream : 0) |
                       (c.kind == 3 ? 8 | kFlagDma : 0);
     if (c.flags & ~known)
         return PROJ_ERR_UNSUPPORTED;
@@ -232,9 +240,50 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
         const int xp = pre == kFlagPreload4 ? 4 : pre == kFlagPreload8 ? 8 : 0;
         if (pre && (!xp || m > xp))
             return PROJ_ERR_UNSUPPORTED;              // both bits, or more tokens than the preload holds
-        const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w, z, xp);
+        const int skm = (c.flags & kFlagStream) ? 1 : 0;
+        const SkinnyVariant *v = find_variant(c.nt, c.rb, c.waves, c.spw, f32w, z, xp, skm);
         if (!v)
             return PROJ_ERR_UNSUPPORTED;
+        if (skm) {
+            // Units: (16-row block, k-step) pairs, dealt in shares of
+            // waves * spw; one token block; every row block covered by at
+            // most kSkMaxParts shares (bounded by ceil(KS / P) + 1).
+            const long long P = (long long)c.waves * c.spw;
+            const long long units = (long long)(ne / kRowsPerBlock) * KS;
+            if (xp || c.rb != 1 || c.ksplit != 1 || ne % kRowsPerBlock != 0 || m > 16 * c.nt || units % P != 0 ||
+                P > KS)                                // a share spans at most two row blocks
+                return PROJ_ERR_UNSUPPORTED;
+            if ((KS + P - 1) / P + 1 > kSkMaxParts)
+                return PROJ_ERR_UNSUPPORTED;
+            if ((long long)(ne / kRowsPerBlock) * kSkMaxParts * c.nt * kWave * (long long)sizeof(f32x4) >
+                (long long)st.pws_bytes)
+                return PROJ_ERR_UNSUPPORTED;
+            const long long grid = units / P;
+            L.fn = v->fn;
+            L.kind = 0;
+            L.grid = (int)grid;
+            L.block = (c.waves + z) * kWave;
+            SkinnyArgs &A = L.sargs;
+            A.wz = st.wz;
+            A.wz_bytes = (uint32_t)((size_t)li.N * li.K * 3 / 2);
+            A.zt0 = st.zt0;
+            A.zt1 = st.zt1;
+            A.zcr = z ? st.zcr : 0;
+            A.zexc = st.zexc;
+            A.wp = st.wp;
+            A.pws = st.pws;
+            A.m = m;
+            A.K = li.K;
+            A.n_eff = ne;
+            A.n_rt = (int)grid;
+            A.n_tt = 1;
+            A.ksplit = 1;
+            A.xcd_remap = (!(c.flags & 1) && grid % 8 == 0) ? 1 : 0;
+            A.giveups = st.giveups;
+            A.drop_publish = (c.flags & kFlagTestLostSplit) ? 1 : 0;
+            A.poll_limit = A.drop_publish ? 1 : kPollLimit;
+            return PROJ_OK;
+        }
         if (c.waves * c.spw * c.ksplit != KS)
             return PROJ_ERR_UNSUPPORTED;
         if (ne % (kRowsPerBlock * c.rb) != 0)
@@ -408,7 +457,7 @@ proj_config plan_default(int layer, int m, int zcr)
 {
     struct Entry {
         int nt, rb, waves, spw, ksplit, z;   // z: read the 12-bit weights when the layer has them
-        int pre;                             // preload the activations (bucket 0 only)
+        int mode;                            // 1: preloaded activations (bucket 0); 2: stream partition
     };
     // [layer][bucket]: bucket 0: m <= 8, 1: m <= 16, 2: m <= 32. Entries
     // are the fastest of every compiled configuration in cold sweeps (a plain
@@ -424,13 +473,15 @@ proj_config plan_default(int layer, int m, int zcr)
     // activations (flags bit 5 / 6): A/B 1.5 / 1.0 / 0.7 us faster on
     // qkv_gate at 1 / 4 / 8 tokens, 0.1-0.2 on the slice; no gain on the
     // pooler, which already runs at the plain read floor there. At 9-16
-    // tokens qkv_gate takes 4-wave workgroups of 16 k-steps per wave with a
-    // 4-way split and the unpooler 4-wave workgroups of two row blocks over
-    // the whole K (in-process A/B at m = 9 / 12 / 16: qkv_gate 0.32 / 0.36 /
-    // 0.16 us faster, unpooler 0.24 / 0.28 / 0.20).
+    // tokens qkv_gate runs the stream partition (flags bit 8: its 144 row
+    // blocks x 256 k-steps dealt to 256 workgroups of 4 waves x 36 k-steps;
+    // A/B against the 4-way split below at m = 9 / 12 / 14 / 16: -0.18 /
+    // -0.44 / -0.48 / -0.64 us in one run, +0.06 / -0.10 / - / -0.32 in
+    // another) and the unpooler 4-wave workgroups of two row blocks over the
+    // whole K (A/B at m = 9 / 12 / 16: 0.24 / 0.28 / 0.20 us faster).
     static const Entry table[PROJ_NUM_LAYERS][3] = {
         /* qkv_gate  144 row blocks, 256 k-steps */
-        {{1, 1, 8, 32, 1, 1, 1}, {1, 1, 4, 16, 4, 1, 0}, {2, 4, 8, 8, 4, 0, 0}},
+        {{1, 1, 8, 32, 1, 1, 1}, {1, 1, 4, 36, 1, 1, 2}, {2, 4, 8, 8, 4, 0, 0}},
         /* o         512 row blocks,  32 k-steps */
         {{1, 2, 8, 4, 1, 0, 0}, {1, 2, 8, 4, 1, 0, 0}, {2, 2, 4, 8, 1, 0, 0}},
         /* pooler    256 row blocks, 256 k-steps */
@@ -463,8 +514,10 @@ proj_config plan_default(int layer, int m, int zcr)
         c.spw = e.spw;
         c.ksplit = e.ksplit;
         c.flags = (e.z && zcr >= 0) ? 4 : 0;
-        if (e.pre)
+        if (e.mode == 1)
             c.flags |= m <= 4 ? kFlagPreload4 : kFlagPreload8;
+        if (e.mode == 2)
+            c.flags |= kFlagStream;
         return c;
     }
     // The router past 32 tokens stays on the skinny kernel: with 16 row
@@ -1099,7 +1152,8 @@ int proj_variant(int i, int *is_f32w, proj_config *cfg)
         c.waves = v->waves;
         c.spw = v->spw;
         c.ksplit = 1;
-        c.flags = (v->z ? 4 : 0) | (v->xp == 4 ? kFlagPreload4 : v->xp == 8 ? kFlagPreload8 : 0);
+        c.flags = (v->z ? 4 : 0) | (v->xp == 4 ? kFlagPreload4 : v->xp == 8 ? kFlagPreload8 : 0) |
+                  (v->skm ? kFlagStream : 0);
         c.block = (v->waves + v->z) * kWave;
         *cfg = c;
     }

@@ -72,6 +72,7 @@ struct SkinnyArgs {
 };
 
 constexpr int kZMaxSlots = 8;    // correction slots per row a 12-bit layer may use
+constexpr int kSkMaxParts = 4;   // stream partition: most shares covering one row block
 
 // XP > 0: at most XP (4 or 8) tokens; each wave loads its whole activation
 // slice (XP rows x SPW k-steps) into registers once instead of one 16-byte
@@ -79,10 +80,21 @@ constexpr int kZMaxSlots = 8;    // correction slots per row a 12-bit layer may 
 // registers with lane permutes. At <= 8 tokens a per-k-step load moves 1 KB
 // per wave for at most 8 rows x 64 useful bytes; dropping them measured
 // 0.7-2.1 us on the 8192-wide layers at one token.
-template <int NT, int RB, int WAVES, int SPW, bool F32W, bool Z = false, int XP = 0>
+// SKM: stream partition. The layer's (16-row block, k-step) pairs, in the
+// packing's own order (row block major), are dealt in equal contiguous shares
+// of WAVES * SPW to the workgroups, so every compute unit streams the same
+// number of weight bytes whatever the layer's row count. A share spans the
+// end of one row block (segment A) and possibly the start of the next (B);
+// the kernel is then instantiated with RB = 2, one accumulator tile per
+// segment, and each k-step feeds its one weight fragment to the accumulator
+// of its own segment. A row block is covered by one to kSkMaxParts shares;
+// their partials are summed by the one the hardware dispatched last (as in
+// the polled split-K).
+template <int NT, int RB, int WAVES, int SPW, bool F32W, bool Z = false, int XP = 0, bool SKM = false>
 __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(SkinnyArgs a)
 {
     static_assert(!(Z && F32W), "12-bit weights are BF16 only");
+    static_assert(!SKM || (RB == 2 && !F32W && XP == 0), "stream partition: two segments, BF16 weights");
     static_assert(XP == 0 || ((XP == 4 || XP == 8) && NT == 1 && !F32W), "preloaded activations: 4 or 8 rows, one token block");
     static_assert(!Z || WAVES > 1, "12-bit variants need a separate wave for the corrections");
     constexpr int U = SPW < 4 ? SPW : 4;             // k-steps per pipeline stage
@@ -114,14 +126,21 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
 
     const int KS = a.K / kStepK;                     // k-steps in the whole row
     const int step0 = (ks * WAVES + wave) * SPW;     // this wave's first k-step
-    const int rb0 = rt * RB;
+    // SKM: this workgroup's share [u0, u0 + WAVES * SPW) of the (row block,
+    // k-step) units; unit v is k-step v - rb * KS of row block rb = v / KS,
+    // and the packed fragment index is v itself.
+    const int u0 = SKM ? L * (WAVES * SPW) : 0;
+    const int rbA = SKM ? u0 / KS : 0;               // row block of segment A
+    const int baseB = (rbA + 1) * KS;                // first unit of segment B
+    const int vw = u0 + wave * SPW;                  // this wave's first unit
+    const int rb0 = SKM ? rbA : rt * RB;
 
     const u32x4 *wbase = reinterpret_cast<const u32x4 *>(a.wp);
     // Each wave walks its k-steps starting at a rotated position, so waves of
     // one workgroup and neighbouring workgroups on an XCD do not all request
     // the same activation lines (and L2 channel) at the same moment.
-    const int rot = (2 * (wave + WAVES * (int)(blockIdx.x / 8))) & (SPW - 1);
-    static_assert((SPW & (SPW - 1)) == 0, "SPW must be a power of two");
+    const int rot = SKM ? 0 : (2 * (wave + WAVES * (int)(blockIdx.x / 8))) & (SPW - 1);
+    static_assert(SKM || (SPW & (SPW - 1)) == 0, "SPW must be a power of two");
 
     // Activations. The MFMA wants lane l to hold token l%16, k = 8*(l/16)+0..7,
     // which as a load would make every lane quad touch four rows (measured
@@ -178,9 +197,17 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
     auto load_stage = [&](int buf, int local) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int step = step0 + ((local + u + rot) & (SPW - 1));
+            int step = step0 + ((local + u + rot) & (SPW - 1));
+            if constexpr (SKM) {
+                const int v = vw + local + u;
+                step = v - (v >= baseB ? baseB : baseB - KS);
+                if constexpr (Z)
+                    wq[buf][u][0] = __builtin_amdgcn_raw_buffer_load_b96(wzr, (uint32_t)((v * kWave + lane) * 12), 0, 0);
+                else
+                    wa[buf][u][0][0] = wbase[(size_t)v * FRAG_U4 + lane];
+            }
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
+            for (int r = 0; r < (SKM ? 0 : RB); ++r) {
                 if constexpr (Z) {
                     wq[buf][u][r] = __builtin_amdgcn_raw_buffer_load_b96(
                         wzr, (uint32_t)((((rb0 + r) * KS + step) * kWave + lane) * 12), 0, 0);
@@ -224,8 +251,20 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
                 }
                 xb[buf][u][t] = tok_ok[t] ? v : u32x4{0u, 0u, 0u, 0u};
             }
+            if constexpr (SKM) {
+                // One fragment per k-step, into the accumulator of its segment
+                // (the other MFMA multiplies zeros: the MFMA units idle here).
+                const bool segA = vw + local + u < baseB;
+                const u32x4 wf = Z ? decode12(wq[buf][u][0], a.zt0, a.zt1) : wa[buf][u][0][0];
+                const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
+                for (int t = 0; t < NT; ++t) {
+                    acc[0][t] = mfma16x16x32(wf, segA ? xb[buf][u][t] : zero, acc[0][t]);
+                    acc[1][t] = mfma16x16x32(wf, segA ? zero : xb[buf][u][t], acc[1][t]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < (SKM ? 0 : RB); ++r) {
                 if constexpr (F32W) {
                     u32x4 hi, mid, lo;
                     split3_f32(wa[buf][u][r][0], wa[buf][u][r][1], hi, mid, lo);
@@ -265,9 +304,14 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
             // gathered for (live slot, token) pairs only, a batch of loads
             // per lane in flight at a time.
             constexpr int EPL = ZSLOTS / kWave;       // slots per lane (at the maximum)
-            const int nslot = 16 * RB * a.zcr;
+            // SKM: rows 0-15 are segment A (k from the share's start to the
+            // row block's end), rows 16-31 segment B (k from 0), present
+            // only when the share reaches the next row block.
+            const int skB = SKM ? max(0, u0 + WAVES * SPW - baseB) : 0;     // units of segment B
+            const int nslot = (SKM ? (skB > 0 ? 32 : 16) : 16 * RB) * a.zcr;
             const uint64_t *src = a.zexc + (size_t)rb0 * 16 * a.zcr;
-            const int k_lo = (ks * WAVES) * SPW * kStepK, k_hi = k_lo + WAVES * SPW * kStepK;
+            const int k_lo = SKM ? (u0 - (baseB - KS)) * kStepK : (ks * WAVES) * SPW * kStepK;
+            const int k_hi = SKM ? min(KS, u0 - (baseB - KS) + WAVES * SPW) * kStepK : k_lo + WAVES * SPW * kStepK;
             const int ntok = min(a.m - tt * ZTOK, ZTOK);   // live tokens of this tile
             uint64_t ent[EPL];
 #pragma unroll
@@ -278,8 +322,8 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
             for (int i = 0; i < EPL; ++i) {
                 const int j = lane + kWave * i;
                 const int k = (int)(ent[i] & 0xffffu);
-                const bool live = j < nslot && k >= k_lo && k < k_hi;
                 const int r = j / a.zcr, c = j - (j / a.zcr) * a.zcr;
+                const bool live = j < nslot && (SKM && r >= 16 ? k < skB * kStepK : k >= k_lo && k < k_hi);
                 const int sl = r * kZMaxSlots + c;
                 if (j < nslot) {
                     zlive[sl] = live ? 1 : 0;
@@ -452,6 +496,116 @@ __global__ __launch_bounds__((WAVES + (Z ? 1 : 0)) * kWave) void skinny_kernel(S
 
     // With WAVES == 1 only the owning lane may read its accumulators.
     constexpr int NTHR = (WAVES + (Z ? 1 : 0)) * kWave;
+    if constexpr (SKM) {
+        // Per segment: the shares covering its row block are first..last
+        // (consecutive logical ids); alone, the share stores the output;
+        // otherwise the one dispatched last sums the parts in share order
+        // (its own from the wave sum), the others publish and move on. A
+        // share waits only on shares with lower hardware ids, which are on
+        // the chip before it, so no wait is circular.
+        // Every publish comes before any wait (two passes over the
+        // segments): a share that reduced first and published after would
+        // make the next share's reduction wait for its reduction, and so on
+        // down the grid.
+        constexpr int SE = NT * kWave;                  // f32x4 per segment tile
+        constexpr uint64_t kEmpty = ~0ull;
+        const int P = WAVES * SPW;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            const int rb = rbA + sg;
+            if (max(rb * KS, u0) >= min((rb + 1) * KS, u0 + P))
+                continue;                               // the share does not reach this row block
+            const int first = (rb * KS) / P, last = ((rb + 1) * KS - 1) / P;
+            const int nparts = last - first + 1, slot = L - first;
+            const int rsg = nparts == 1 ? slot : reducing_split(first, 1, nparts, G, a.xcd_remap != 0);
+            if ((slot == rsg) != (pass == 1))
+                continue;                               // pass 0: publish; pass 1: store or reduce
+            if (nparts == 1) {
+                for (int e = threadIdx.x; e < SE; e += NTHR)
+                    store_out(sg * SE + e, wave_sum(sg * SE + e));
+                continue;
+            }
+            uint64_t *parts = a.pws + (size_t)rb * kSkMaxParts * SE * 2;   // slot p: SE units of two words
+            if (slot != rsg) {
+                if (!a.drop_publish)
+                    for (int e = threadIdx.x; e < SE; e += NTHR) {
+                        const u32x4 u = publishable(__builtin_bit_cast(u32x4, wave_sum(sg * SE + e)));
+                        uint64_t *d = parts + ((size_t)slot * SE + e) * 2;
+                        __hip_atomic_store(d, (uint64_t)u.x | ((uint64_t)u.y << 32), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(d + 1, (uint64_t)u.z | ((uint64_t)u.w << 32), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                continue;
+            }
+            for (int e0 = 0; e0 < SE; e0 += NTHR) {
+                const int e = e0 + (int)threadIdx.x;
+                const bool mine = e < SE;
+                // Every other part's two words at once, then the ones still
+                // empty again, bounded as in the polled split-K.
+                uint64_t w[kSkMaxParts][2];
+#pragma unroll
+                for (int q = 0; q < kSkMaxParts; ++q)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        w[q][h] = (mine && q < nparts && q != slot)
+                                      ? __hip_atomic_load(parts + ((size_t)q * SE + e) * 2 + h, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT)
+                                      : 0ull;
+                for (int poll = 0;; ++poll) {
+                    bool miss = false;
+#pragma unroll
+                    for (int q = 0; q < kSkMaxParts; ++q)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            miss |= w[q][h] == kEmpty;
+                    if (!__any(miss))
+                        break;
+                    if (poll >= a.poll_limit) {
+#pragma unroll
+                        for (int q = 0; q < kSkMaxParts; ++q)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+                                w[q][h] = w[q][h] == kEmpty ? 0x7fc000007fc00000ull : w[q][h];
+                        if (lane == 0)
+                            __hip_atomic_fetch_add(a.giveups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+#pragma unroll
+                    for (int q = 0; q < kSkMaxParts; ++q)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            if (w[q][h] == kEmpty)
+                                w[q][h] = __hip_atomic_load(parts + ((size_t)q * SE + e) * 2 + h, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (mine) {
+                    const f32x4 own = wave_sum(sg * SE + e);
+                    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int q = 0; q < kSkMaxParts; ++q) {
+                        if (q >= nparts)
+                            break;
+                        if (q == slot) {
+                            v += own;
+                            continue;
+                        }
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            __hip_atomic_store(parts + ((size_t)q * SE + e) * 2 + h, kEmpty, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        const u32x4 u = {(uint32_t)w[q][0], (uint32_t)(w[q][0] >> 32), (uint32_t)w[q][1],
+                                         (uint32_t)(w[q][1] >> 32)};
+                        v += __builtin_bit_cast(f32x4, u);
+                    }
+                    store_out(sg * SE + e, v);
+                }
+            }
+        }
+        return;
+    }
     if (a.ksplit == 1) {
         if constexpr (WAVES > 1) {
             for (int e = threadIdx.x; e < ELEMS; e += NTHR)

@@ -14,6 +14,7 @@ struct SkinnyVariant {
     const void *fn;   // __global__ void (SkinnyArgs)
     int z;            // 1: reads the 12-bit weights (one extra wave per workgroup)
     int xp;           // 4 or 8: activations preloaded per wave (at most that many tokens); 0: loaded per k-step
+    int skm;          // 1: stream partition (skinny_kernel's SKM; rb is 1 in the configuration)
 };
 
 // Tiled (large-m) kernel variants: BMB x BNB blocks of 16 per workgroup, WR waves
@@ -59,6 +60,8 @@ extern const SkinnyVariant kSkinnyPartF32[];
 extern const int kSkinnyPartF32Count;
 extern const SkinnyVariant kSkinnyPartZ[];
 extern const int kSkinnyPartZCount;
+extern const SkinnyVariant kSkinnyPartStream[];
+extern const int kSkinnyPartStreamCount;
 extern const TiledVariant kTiledVariants[];
 extern const int kTiledVariantCount;
 extern const WideVariant kWideVariants[];

@@ -90,6 +90,13 @@ def test_dispatch_plans_tile_every_layer(lib):
                 assert cfg.spw * 2048 == k
                 assert ne % cfg.rb == 0 and cfg.grid == ne // cfg.rb
                 continue
+            if cfg.kind == 0 and cfg.flags & 256:
+                # stream partition: qkv_gate at 9-16 tokens, its (row block, k-step) units dealt in
+                # shares of waves x spw, one share per workgroup
+                assert name == "qkv_gate" and 8 < m <= 16 and (cfg.nt, cfg.rb, cfg.ksplit) == (1, 1, 1)
+                units = ne // 16 * (k // 32)
+                assert units % (cfg.waves * cfg.spw) == 0 and cfg.grid == units // (cfg.waves * cfg.spw)
+                continue
             if cfg.kind == 0:
                 assert cfg.waves * cfg.spw * cfg.ksplit == k // 32
                 # preloaded activations: one 16-token block, at most 4 (bit 5) or 8 (bit 6) tokens
@@ -125,7 +132,7 @@ def test_variant_registry(lib):
     seen = set()
     for i in range(nv):
         f32, cfg = binding.proj_variant(i)
-        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags & (4 | 32 | 64 | 128))
+        key = (f32, cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags & (4 | 32 | 64 | 128 | 256))
         assert key not in seen
         seen.add(key)
     with pytest.raises(binding.ProjError):

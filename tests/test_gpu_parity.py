@@ -463,6 +463,72 @@ def test_split_giveup_is_counted_and_cleaned(layer, m):
     assert binding.proj_split_giveups(layer) == 0
 
 
+# (token blocks, waves, k-steps per wave, 12-bit flag): every compiled stream-partition variant.
+_SK_CFGS = [(nt, w, s, z) for (nt, w, s) in ((1, 4, 36), (1, 6, 24), (1, 9, 16), (1, 12, 12), (2, 6, 24), (2, 9, 16))
+            for z in (0, 4)] + [(1, 2, 72, 4), (1, 3, 48, 4), (2, 4, 36, 4), (2, 3, 48, 4), (2, 2, 72, 4)]
+
+
+@pytest.mark.parametrize("nt,waves,spw,z", _SK_CFGS)
+def test_stream_partition(nt, waves, spw, z):
+    """The skinny kernel's stream partition (flags bit 8): qkv_gate's 144 row
+    blocks x 256 k-steps dealt in 256 shares of waves x spw = 144 units, a
+    share spanning the end of one row block and the start of the next, each
+    row block's two or three parts summed by the share dispatched last. Exact
+    against the oracle (BF16 and 12-bit weights, one and two token blocks,
+    ragged m), bit-identical on a rerun, and no reducer gives up."""
+    p = prepared(0)
+    layer = "qkv_gate"
+    mk = binding.ProjConfig.make
+    cfg = mk(kind=0, nt=nt, rb=1, waves=waves, spw=spw, ksplit=1, flags=256 | z)
+    for m in ((1, 7, 16) if nt == 1 else (17, 24, 32)):
+        xs = make_x(layer, m, seed=2500 + m, outliers=True)
+        say("stream partition", cfg.as_dict(), "m=%d" % m)
+        got = run_layer(layer, xs.bits, cfg=cfg)
+        r = compare(layer, got, p.w[layer], xs)
+        assert r.ok, (m, r)
+        assert np.array_equal(run_layer(layer, xs.bits, cfg=cfg), got)
+    assert binding.proj_split_giveups(layer) == 0
+
+
+def test_stream_partition_rejects_what_it_cannot_cover():
+    """Host-side checks: too many tokens for its token blocks, a share count
+    that does not divide the layer's units, another flag with it."""
+    prepared(0)
+    mk = binding.ProjConfig.make
+    x = to_device_x(make_x("qkv_gate", 17, seed=3).bits)
+    out = binding.new_out("qkv_gate", 17)
+    with pytest.raises(binding.ProjError):                       # 17 tokens, one token block
+        binding.proj_run_config("qkv_gate", x, 17, out, mk(kind=0, nt=1, rb=1, waves=6, spw=24, ksplit=1, flags=256))
+    xo = to_device_x(make_x("o", 4, seed=3).bits)
+    with pytest.raises(binding.ProjError):                       # o: 512 x 32 units, not a multiple of 144
+        binding.proj_run_config("o", xo, 4, binding.new_out("o", 4),
+                                mk(kind=0, nt=1, rb=1, waves=6, spw=24, ksplit=1, flags=256))
+    for bad in (mk(kind=0, nt=1, rb=1, waves=6, spw=24, ksplit=2, flags=256),
+                mk(kind=0, nt=1, rb=2, waves=6, spw=24, ksplit=1, flags=256),
+                mk(kind=0, nt=1, rb=1, waves=6, spw=24, ksplit=1, flags=256 | 32)):
+        with pytest.raises(binding.ProjError):
+            binding.proj_run_config("qkv_gate", x, 4, out, bad)
+
+
+def test_stream_partition_giveup_is_counted_and_cleaned():
+    """With the test flag (bit 4) the shares that do not reduce publish
+    nothing and each reducer polls once: outputs of row blocks with several
+    parts read NaN, one give-up per reducer wave, the marks restored, and the
+    same configuration without the flag is exact afterwards."""
+    p = prepared(0)
+    layer = "qkv_gate"
+    assert binding.proj_split_giveups(layer, reset=True) == 0
+    mk = binding.ProjConfig.make
+    xs = make_x(layer, 16, seed=2600, outliers=True)
+    got = run_layer(layer, xs.bits, cfg=mk(kind=0, nt=1, rb=1, waves=6, spw=24, ksplit=1, flags=256 | 16 | 4))
+    assert np.isnan(got).all()              # every row block of qkv_gate has two or three parts
+    assert binding.proj_split_giveups(layer) > 0
+    got = run_layer(layer, xs.bits, cfg=mk(kind=0, nt=1, rb=1, waves=6, spw=24, ksplit=1, flags=256 | 4))
+    assert compare(layer, got, p.w[layer], xs).ok
+    binding.proj_split_giveups(layer, reset=True)
+    assert binding.proj_split_giveups(layer) == 0
+
+
 def test_no_split_giveups_in_normal_use():
     """No polled split-K reducer gives up in normal use: not in prepare's
     warm-up launches and not over every load's plans (a give-up there would

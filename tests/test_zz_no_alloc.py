@@ -5,8 +5,8 @@ Checked against proj_run on the same inputs (bit-identical: same kernels, same
 summation order) and against the oracle, for two calls in a row on one layer,
 the second with fewer tokens (the array keeps the first call's state), over
 plans with every kind of split-K scratch: polled partials (router, qkv_gate at
-32 tokens), counted partials with arrival counters (wide-tile splits at 130,
-200, 256 and 300 tokens), and none.
+32 tokens, qkv_gate's stream partition at 9-16 tokens), counted partials with
+arrival counters (wide-tile splits at 130, 200, 256 and 300 tokens), and none.
 """
 
 import numpy as np
@@ -41,9 +41,9 @@ def _run(fn, layer, xd, m):
     return out
 
 
-@pytest.mark.parametrize("layer,m1,m2", [("router", 32, 16), ("qkv_gate", 32, 17), ("pooler", 256, 130),
-                                         ("qkv_gate", 256, 200), ("o", 300, 64), ("unpooler", 9, 5),
-                                         ("router", 1024, 300)])
+@pytest.mark.parametrize("layer,m1,m2", [("router", 32, 16), ("qkv_gate", 32, 17), ("qkv_gate", 16, 9),
+                                         ("pooler", 256, 130), ("qkv_gate", 256, 200), ("o", 300, 64),
+                                         ("unpooler", 9, 5), ("router", 1024, 300)])
 def test_noalloc_matches_proj_run(layer, m1, m2):
     w = _weights(layer)
     for m in (m1, m2):
