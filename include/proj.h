@@ -237,6 +237,14 @@ int proj_last_hip_error(void);
  *             bit 7 set (kind 3, BF16 weights): activations move from memory
  *             straight into the LDS ring by DMA instead of through registers;
  *             same arithmetic and summation order as with the bit clear.
+ *             bit 8 set (kind 0, rb 1, ksplit 1, m <= 16 * nt): stream
+ *             partition. The layer's (16-row block, k-step) pairs are dealt
+ *             in equal contiguous shares of waves * spw to the workgroups
+ *             (grid = row blocks * K/32 / (waves * spw), which must divide
+ *             exactly, with waves * spw <= K/32); each row block's parts
+ *             (at most 4) are summed by the share dispatched last (polled,
+ *             bounded, counted like kind 0's split). Compiled for
+ *             waves x spw = 144 (qkv_gate: 256 workgroups).
  *             Other bits, or a bit the kind does not use, are rejected.
  * proj_plan fills the configuration proj_run would use; proj_run_config runs
  * an explicit one and returns PROJ_ERR_UNSUPPORTED if it is not compiled or
@@ -252,7 +260,7 @@ typedef struct {
     int flags;     /* bit 0: keep hardware workgroup order (no XCD grouping); bit 2: 12-bit weights;
                       bit 3: stream mode (kind 3); bit 4: test-only lost split (kind 0);
                       bits 5 / 6: activations preloaded for <= 4 / <= 8 tokens (kind 0);
-                      bit 7: activations by LDS DMA (kind 3) */
+                      bit 7: activations by LDS DMA (kind 3); bit 8: stream partition (kind 0) */
     int grid;      /* filled by proj_plan: workgroups launched */
     int block;     /* filled by proj_plan: threads per workgroup */
 } proj_config;
