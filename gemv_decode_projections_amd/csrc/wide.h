@@ -420,8 +420,11 @@ __global__ __launch_bounds__(WAVES * kWave) void wide_kernel(WideArgs a)
             if (!s_last)
                 return;
             // Sum in slot order; this workgroup's own part comes from
-            // registers (the same bits it published). CH parts are gathered
-            // per round with every load in flight.
+            // registers (the same bits it published) and only the other
+            // nparts - 1 are read, CH per round with every load in flight.
+            // The loads that pad the last round address the workspace
+            // descriptor's end: out of its range, so they return zero
+            // without a memory access, and they are never summed.
             constexpr int CH = (RBW * BNB >= 16) ? 2 : (RBW * BNB >= 8 ? 4 : 8);
             f32x4 sum[RBW][BNB];
 #pragma unroll
@@ -429,29 +432,49 @@ __global__ __launch_bounds__(WAVES * kWave) void wide_kernel(WideArgs a)
 #pragma unroll
                 for (int t = 0; t < BNB; ++t)
                     sum[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < nparts; c0 += CH) {
+            const int nother = nparts - 1;
+            bool own_added = false;
+            for (int c0 = 0; c0 < nother; c0 += CH) {
                 u32x4 part[CH][RBW][BNB];
 #pragma unroll
                 for (int ci = 0; ci < CH; ++ci) {
-                    const int sp = min(c0 + ci, nparts - 1);   // past the end: re-read, never summed
+                    const int o = c0 + ci;                     // o-th part other than this one
+                    const int sp = o + (o >= slot ? 1 : 0);
+                    const uint32_t base = o < nother ? tile_off + (uint32_t)sp * TILE_U * 16u : a.ws_bytes;
 #pragma unroll
                     for (int r = 0; r < RBW; ++r)
 #pragma unroll
                         for (int t = 0; t < BNB; ++t)
                             part[ci][r][t] = __builtin_amdgcn_raw_buffer_load_b128(
-                                ws, tile_off + ((uint32_t)sp * TILE_U + unit_of(r, t)) * 16u, 0, kCoherent);
+                                ws, base + (uint32_t)unit_of(r, t) * 16u, 0, kCoherent);
                 }
 #pragma unroll
                 for (int ci = 0; ci < CH; ++ci) {
-                    const int sp = c0 + ci;
-                    if (sp >= nparts)
+                    const int o = c0 + ci;
+                    if (o >= nother)
                         break;
+                    const int sp = o + (o >= slot ? 1 : 0);
+                    if (!own_added && slot < sp) {
+#pragma unroll
+                        for (int r = 0; r < RBW; ++r)
+#pragma unroll
+                            for (int t = 0; t < BNB; ++t)
+                                sum[r][t] += acc[r][t];
+                        own_added = true;
+                    }
 #pragma unroll
                     for (int r = 0; r < RBW; ++r)
 #pragma unroll
                         for (int t = 0; t < BNB; ++t)
-                            sum[r][t] += (sp == slot) ? acc[r][t] : __builtin_bit_cast(f32x4, part[ci][r][t]);
+                            sum[r][t] += __builtin_bit_cast(f32x4, part[ci][r][t]);
                 }
+            }
+            if (!own_added) {
+#pragma unroll
+                for (int r = 0; r < RBW; ++r)
+#pragma unroll
+                    for (int t = 0; t < BNB; ++t)
+                        sum[r][t] += acc[r][t];
             }
 #pragma unroll
             for (int r = 0; r < RBW; ++r)
