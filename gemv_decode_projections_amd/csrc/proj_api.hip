@@ -203,7 +203,7 @@ const SkinnyVariant *variant_at(int i)
     return nullptr;
 }
 
-// Resolved launch of one configuration (one of the two argument blocks is used).
+// Resolved launch of one configuration (only the argument block of its kind is used).
 struct Launch {
     const void *fn;
     int kind;
@@ -227,7 +227,8 @@ int resolve(int layer, int m, const proj_config &c, Launch &L, const LayerState 
         return PROJ_ERR_UNSUPPORTED;
     // Flag bits each kind understands: 0 placement (all), 2 12-bit weights
     // (kind 0), 3 stream mode (kind 3), 4 the test-only lost split (kind 0),
-    // 5 / 6 preloaded activations (kind 0), 7 activations by LDS DMA (kind 3).
+    // 5 / 6 preloaded activations (kind 0), 7 activations by LDS DMA (kind 3),
+    // 8 the stream partition (kind 0).
     const int known = 1 | (c.kind == 0 ? 4 | kFlagTestLostSplit | kFlagPreload4 | kFlagPreload8 | kFlagStream : 0) |
                       (c.kind == 3 ? 8 | kFlagDma : 0);
     if (c.flags & ~known)
