@@ -466,14 +466,13 @@ proj_config plan_default(int layer, int m, int zcr)
     // Infinity Cache), kept where they beat the next one by more than the
     // sweep's noise. The 12-bit form pays wherever the weight stream is long
     // (qkv_gate and pooler to 16 tokens, the full unpooler to 32); o's short
-    // stream does not hide the correction wave. At 17-32 tokens qkv_gate and
-    // the pooler read less per workgroup with 64-row tiles over both token
-    // blocks and a 4-way K split (each workgroup reads a quarter of x instead
-    // of all of it): in-process A/B 0.5 us faster at 32 tokens, 1.0-1.3 at 24.
+    // stream does not hide the correction wave. Bucket 2 of qkv_gate and the
+    // pooler (64-row tiles over both token blocks, a 4-way K split) is not
+    // reached: the wide-tile rule below takes them at 17-32 tokens.
     // Up to 8 tokens qkv_gate and the unpooler slice preload each wave's
     // activations (flags bit 5 / 6): A/B 1.5 / 1.0 / 0.7 us faster on
     // qkv_gate at 1 / 4 / 8 tokens, 0.1-0.2 on the slice; no gain on the
-    // pooler, which already runs at the plain read floor there. At 9-16
+    // pooler, which already runs at the plain read floor there. At 9-15
     // tokens qkv_gate runs the stream partition (flags bit 8: its 144 row
     // blocks x 256 k-steps dealt to 256 workgroups of 4 waves x 36 k-steps;
     // A/B against the 4-way split below at m = 9 / 12 / 14 / 16: -0.18 /
@@ -517,6 +516,26 @@ proj_config plan_default(int layer, int m, int zcr)
         c.spw = 32;
         c.ksplit = 2;
         c.flags = 4;
+        return c;
+    }
+    // qkv_gate at 16-32 tokens and the pooler at 17-32 on the wide-tile
+    // kernel (kind 3): 64-row tiles of 16 tokens (m = 16) or 32 tokens, the
+    // activations staged once per workgroup in LDS instead of loaded by every
+    // wave, an arrival-counted K split. In-process cold A/B against the
+    // skinny plans (us): qkv_gate m = 16 / 17 / 24 / 32 11.88 / 13.76 /
+    // 14.62 / 15.62 -> 11.66 / 12.26 / 12.32 / 12.48 (the stream partition
+    // stays ahead at 9-13 tokens, a tie at 14); pooler m = 17 / 24 / 28 / 32
+    // 17.12 / 17.20 / 17.38 / 17.74 -> 16.86 / 16.76 / 16.92 / 16.84 (within
+    // noise at 20). The unpooler (29-32) and o measured no gain.
+    if ((layer == PROJ_QKV_GATE && m >= 16 && m <= 32) || (layer == PROJ_POOLER && m >= 17 && m <= 32)) {
+        const bool qkv = layer == PROJ_QKV_GATE;
+        c.kind = 3;
+        c.nt = m <= 16 ? 1 : 2;
+        c.rb = 4;
+        c.waves = 4;
+        c.spw = qkv ? 16 : 8;
+        c.ksplit = qkv ? 6 : 4;
+        c.flags = qkv ? 0 : kFlagDma;
         return c;
     }
     if (m <= 32) {

@@ -12,6 +12,8 @@ namespace gdp {
 
 const WideVariant kWideDmaVariants[] = {
     GDP_WIDE_DMA(1, 2, 8, 4)
+    GDP_WIDE_DMA(1, 1, 16, 4)
+    GDP_WIDE_DMA(1, 2, 16, 4)
     GDP_WIDE_DMA(1, 4, 8, 4)
     GDP_WIDE_DMA(1, 8, 8, 4)
     GDP_WIDE_DMA(2, 2, 8, 4)

@@ -16,6 +16,8 @@ namespace gdp {
 
 const WideVariant kWideVariants[] = {
     GDP_WIDE(1, 2, 8, 0)
+    GDP_WIDE(1, 1, 16, 0)
+    GDP_WIDE(1, 2, 16, 0)
     GDP_WIDE(1, 4, 8, 0)
     GDP_WIDE(1, 8, 8, 0)
     GDP_WIDE(2, 2, 8, 0)

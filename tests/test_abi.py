@@ -91,9 +91,9 @@ def test_dispatch_plans_tile_every_layer(lib):
                 assert ne % cfg.rb == 0 and cfg.grid == ne // cfg.rb
                 continue
             if cfg.kind == 0 and cfg.flags & 256:
-                # stream partition: qkv_gate at 9-16 tokens, its (row block, k-step) units dealt in
+                # stream partition: qkv_gate at 9-15 tokens, its (row block, k-step) units dealt in
                 # shares of waves x spw, one share per workgroup
-                assert name == "qkv_gate" and 8 < m <= 16 and (cfg.nt, cfg.rb, cfg.ksplit) == (1, 1, 1)
+                assert name == "qkv_gate" and 8 < m <= 15 and (cfg.nt, cfg.rb, cfg.ksplit) == (1, 1, 1)
                 units = ne // 16 * (k // 32)
                 assert units % (cfg.waves * cfg.spw) == 0 and cfg.grid == units // (cfg.waves * cfg.spw)
                 continue
@@ -107,6 +107,13 @@ def test_dispatch_plans_tile_every_layer(lib):
             elif cfg.kind == 1:
                 assert (k // 32) % (cfg.spw * cfg.ksplit) == 0
                 assert m > 32
+            elif m <= 32:
+                # qkv_gate at 16-32 tokens and the pooler at 17-32 on wide tiles: 64 rows, one
+                # (m = 16) or two token blocks, 4 waves, a 6- / 4-way split, the pooler's by LDS DMA
+                qkv = name == "qkv_gate"
+                assert cfg.kind == 3 and ((qkv and m >= 16) or (name == "pooler" and m >= 17))
+                assert (cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.ksplit, cfg.flags) == \
+                    (1 if m <= 16 else 2, 4, 4, 16 if qkv else 8, 6 if qkv else 4, 0 if qkv else 128)
             else:
                 # wide tiles: 4 waves (8 past 256 tokens, 256-row tiles), whole row blocks per
                 # wave, any split up to one super-step each

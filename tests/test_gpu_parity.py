@@ -157,8 +157,10 @@ def test_every_compiled_variant(case):
         ms = [1, 3, 4] if flags & 32 else [1, 5, 8]     # preloaded activations: at most 4 / 8 tokens
     elif kind == 0:
         ms = [1, 16 * nt - 3, 16 * nt + 5]
-    elif kind in (1, 3):
+    elif kind == 1:
         ms = [33, 16 * nt + 5, 3 * 16 * nt - 7]
+    elif kind == 3:
+        ms = [1, 16 * nt - 3, 33, 16 * nt + 5, 3 * 16 * nt - 7]   # dispatched from 16 tokens up
     else:
         ms = [1, nt // 2 + 1, nt]      # row-dot: up to its token capacity
     for m in sorted(set(ms)):
