@@ -576,19 +576,9 @@ proj_config plan_default(int layer, int m, int zcr)
         }
         return c;
     }
-    // qkv_gate just past 32 tokens: the 12-bit skinny kernel over 16-token
-    // tiles (each tile re-reads the 12-bit stream, mostly from L2) beat the
-    // tiled kernels up to 48 tokens (m = 33 / 48: 12.4 / 12.7 us against
-    // 13.4 / 13.5) and lost at 64 (17.2 against 13.3).
-    if (layer == PROJ_QKV_GATE && m <= 48 && zcr >= 0) {
-        c.nt = 1;
-        c.rb = 2;
-        c.waves = 8;
-        c.spw = 32;
-        c.ksplit = 1;
-        c.flags = 4;
-        return c;
-    }
+    // (qkv_gate at 33-48 tokens once ran the 12-bit skinny kernel over
+    // 16-token tiles; with the weights really cold the wide tiles below are
+    // faster: m = 33 / 40 / 48 16.5 / 16.6 / 16.8 -> 14.1 / 14.2 / 14.4 us.)
     // Larger m: the tiled kernel (kind 1) or the wide-tile kernel (kind 3),
     // picked per layer from measured cold-cache sweeps. Buckets: m <= 64,
     // m <= 128, m <= 256, larger. Entries: kind, 16-row blocks per tile (rb),
