@@ -1,7 +1,9 @@
 // Wide-tile MFMA kernel: out = x @ W^T when many tokens share each weight
-// byte (m >= 33; the pages' verify loads run m = 128 and 256, guide ch. 1
-// "The problem, the judge and the speed of light", §1.2, and only there does
-// the math approach the memory time, §1.7).
+// byte (m >= 33, and from 16-17 tokens on qkv_gate and the pooler, where
+// staging the activations once per workgroup beats loading them per wave;
+// the pages' verify loads run m = 128 and 256, guide ch. 1 "The problem, the
+// judge and the speed of light", §1.2, and only there does the math approach
+// the memory time, §1.7).
 //
 // The report "Muse Spark Open Kernel Challenge - muse_bf16_proj" (round 4)
 // traced its dense-layer losses to activations re-read by every row tile and
