@@ -193,9 +193,10 @@ int proj_last_hip_error(void);
  *               into registers, activation tiles staged in LDS), 2 = row-dot
  *               kernel (m <= 8, router and the unpooler's 1024-row slice
  *               only: whole rows per workgroup from a row-major weight copy,
- *               FP32 multiply-adds), 3 = wide-tile MFMA kernel (large m;
- *               4 or 8 waves, up to 128 x 128 tiles, K split unevenly over up to
- *               KS/2 workgroups, KS/4 at prefetch depth 16)
+ *               FP32 multiply-adds), 3 = wide-tile MFMA kernel (activations
+ *               staged once per workgroup in LDS; 4 or 8 waves, tiles of 64-256
+ *               rows x 16-128 tokens, K split unevenly over up to KS/2
+ *               workgroups, KS/4 at prefetch depth 16)
  *   nt        token sub-tiles of 16 per workgroup (kinds 0, 1, 3); largest token
  *             count of the variant (kind 2)
  *   rb        16-row blocks per workgroup (kinds 0, 1, 3; a multiple of 4
