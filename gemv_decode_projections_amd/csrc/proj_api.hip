@@ -552,28 +552,40 @@ proj_config plan_default(int layer, int m, int zcr)
             c.flags |= kFlagStream;
         return c;
     }
-    // The router past 32 tokens stays on the skinny kernel: with 16 row
+    // The router at 33-256 tokens stays on the skinny kernel: with 16 row
     // blocks the tiled kernels' 64-row tiles leave most compute units idle
     // or need deep K splits (measured 12-15 us against 8-13.5 here). Two
     // 16-token blocks per workgroup from 65 tokens, two row blocks from 129.
+    // Past 256 tokens: the wide-tile kernel's FP32-weight tiles (64 rows x 64
+    // tokens, 128 past 1024 tokens; the exact three-part split as in the
+    // skinny kernel), K split over up to 8 workgroups, the grid filled to 512
+    // (64-token tiles) or 256 workgroups. In-process cold A/B against the
+    // skinny plans (us): m = 512 / 896 / 1500 / 2048 / 4096 / 8192 21.8 /
+    // 32.6 / 49.9 / 63.8 / 118.2 / 231.5 -> 20.3 / 25.0 / 32.9 / 39.6 / 68.1
+    // / 126.3 (a tie at 257-300).
+    if (layer == PROJ_ROUTER && m > 256) {
+        const int nt = m <= 1024 ? 4 : 8;
+        const long tiles = (long)(kLayers[layer].N / 64) * ((m + 16 * nt - 1) / (16 * nt));
+        c.kind = 3;
+        c.nt = nt;
+        c.rb = 4;
+        c.waves = 4;
+        c.spw = 4;
+        int ks = (int)std::max(1L, std::min(8L, (nt == 4 ? 512 : 256) / tiles));
+        while (ks > 1 && tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes)
+            --ks;
+        c.ksplit = ks;
+        c.flags = 0;
+        return c;
+    }
     if (layer == PROJ_ROUTER) {
-        static const Entry rtable[4] = {
-            {1, 1, 16, 4, 4, 0}, {2, 1, 16, 4, 4, 0}, {2, 2, 16, 4, 4, 0}, {2, 2, 4, 16, 4, 0}};
-        const Entry &e = rtable[m <= 64 ? 0 : m <= 128 ? 1 : m <= 256 ? 2 : 3];
+        static const Entry rtable[3] = {{1, 1, 16, 4, 4, 0}, {2, 1, 16, 4, 4, 0}, {2, 2, 16, 4, 4, 0}};
+        const Entry &e = rtable[m <= 64 ? 0 : m <= 128 ? 1 : 2];
         c.nt = e.nt;
         c.rb = e.rb;
         c.waves = e.waves;
         c.spw = e.spw;
         c.ksplit = e.ksplit;
-        // Past 8192 tokens the split partials would overflow the workspace:
-        // the whole K range in one workgroup (16 waves of 16 k-steps).
-        const long long parts = (long long)(kLayers[layer].N / (16 * e.rb)) * ((m + 16 * e.nt - 1) / (16 * e.nt)) *
-                                e.ksplit * e.rb * e.nt * kWave * (long long)sizeof(f32x4);
-        if (parts > (long long)kWsBytes) {
-            c.waves = 16;
-            c.spw = 16;
-            c.ksplit = 1;
-        }
         return c;
     }
     // (qkv_gate at 33-48 tokens once ran the 12-bit skinny kernel over
@@ -581,13 +593,10 @@ proj_config plan_default(int layer, int m, int zcr)
     // faster: m = 33 / 40 / 48 16.5 / 16.6 / 16.8 -> 14.1 / 14.2 / 14.4 us.)
     // Larger m: the tiled kernel (kind 1) or the wide-tile kernel (kind 3),
     // picked per layer from measured cold-cache sweeps. Buckets: m <= 64,
-    // m <= 128, m <= 256, larger. Entries: kind, 16-row blocks per tile (rb),
-    // 16-token blocks (nt), weight prefetch depth in k-steps, K split. Past
-    // 256 tokens a tile takes 128 tokens once 64-token tiles would give more
-    // than one workgroup per compute unit (the deep-prefetch variants hold 64
-    // tokens, so the depth drops to 8 there), and the split shrinks until the
-    // grid is at most ~3 workgroups per compute unit and the partials fit the
-    // workspace. A split of 0 means: as many splits (at most 4) as keep the
+    // m <= 128, m <= 256 (past 256 tokens the rule further down). Entries:
+    // kind, 16-row blocks per tile (rb), 16-token blocks (nt), weight
+    // prefetch depth in k-steps, K split; the split shrinks until the partials
+    // fit the workspace. A split of 0 means: as many splits (at most 4) as keep the
     // grid within one workgroup per compute unit (a grid past 256 measured
     // far slower: qkv_gate m = 130 with 64-token tiles took 18.7 us at 4
     // splits, 216 workgroups, 32.4 at 5, 270 workgroups, and 24.5 at 3).
@@ -600,26 +609,15 @@ proj_config plan_default(int layer, int m, int zcr)
     struct TEntry {
         int kind, rb, nt, waves, depth, ksplit, dma;
     };
-    // Measured in the same cold sweeps (m = 64, 128, 256); bucket 3 (past 256
-    // tokens) keeps its split rule below.
-    static const TEntry ttable[PROJ_ROUTER][4] = {   // the four BF16 layers
-        /* qkv_gate */ {{3, 4, 4, 4, 16, 6, 0}, {3, 4, 4, 4, 16, 3, 0}, {3, 8, 4, 4, 16, 0, 1}, {3, 8, 4, 4, 16, 0, 0}},
-        /* o        */ {{1, 4, 2, 4, 16, 1, 0}, {1, 8, 2, 4, 8, 1, 0}, {3, 8, 4, 4, 4, 0, 0}, {3, 8, 4, 4, 4, 0, 0}},
-        /* pooler   */ {{3, 4, 4, 4, 8, 4, 0}, {3, 8, 4, 4, 8, 4, 1}, {3, 8, 8, 8, 8, 0, 1}, {3, 8, 4, 4, 16, 0, 1}},
-        /* unpooler */ {{1, 4, 2, 4, 16, 1, 0}, {3, 4, 4, 4, 16, 1, 0}, {3, 8, 4, 4, 16, 0, 1}, {3, 8, 4, 4, 16, 0, 1}},
+    // Measured in the same cold sweeps (m = 64, 128, 256).
+    static const TEntry ttable[PROJ_ROUTER][3] = {   // the four BF16 layers
+        /* qkv_gate */ {{3, 4, 4, 4, 16, 6, 0}, {3, 4, 4, 4, 16, 3, 0}, {3, 8, 4, 4, 16, 0, 1}},
+        /* o        */ {{1, 4, 2, 4, 16, 1, 0}, {1, 8, 2, 4, 8, 1, 0}, {3, 8, 4, 4, 4, 0, 0}},
+        /* pooler   */ {{3, 4, 4, 4, 8, 4, 0}, {3, 8, 4, 4, 8, 4, 1}, {3, 8, 8, 8, 8, 0, 1}},
+        /* unpooler */ {{1, 4, 2, 4, 16, 1, 0}, {3, 4, 4, 4, 16, 1, 0}, {3, 8, 4, 4, 16, 0, 1}},
     };
     const int ne = n_eff_of(layer, m);
-    // Past 256 tokens the 8-wave wide kernel (two waves per SIMD) holds
-    // 256-row tiles: 64 tokens wide while that still gives at least 160
-    // workgroups (with the split rule below), else 128 tokens wide while the
-    // grid stays within 512 workgroups (256 for o); past that the 4-wave
-    // rule further down. Measured against the 4-wave rule (us): qkv_gate
-    // m = 300 / 512 / 700 / 1000 / 2048 30.9 / 36.8 / 57.0 / 60.8 / 120.2 ->
-    // 25.6 / 30.0 / 39.9 / 47.3 / 84.8; pooler m = 300 / 700 / 2048 34.7 / 61.6 /
-    // 128.5 -> 29.7 / 56.0 / 109.2; unpooler m = 300 / 700 / 1000 / 2048 32.1 /
-    // 65.2 / 67.4 / 136.9 -> 29.7 / 47.9 / 57.9 / 114.0; o m = 300 / 700 / 1000
-    // 12.2 / 20.5 / 21.9 -> 11.4 / 18.5 / 20.9.
-    // The pooler at 129-192 tokens: the same 256 x 64 tiles with 5 splits
+    // The pooler at 129-192 tokens: 256 x 64 tiles on 8 waves with 5 splits
     // (240 workgroups) beat its 128 x 64 tiles with 2 (m = 130 / 160 / 192:
     // 24.6 / 24.9 / 25.6 -> 23.6 / 24.2 / 24.3 us); the other layers, and the
     // pooler at 193-256, measured no gain.
@@ -630,50 +628,70 @@ proj_config plan_default(int layer, int m, int zcr)
         c.waves = 8;
         c.spw = 8;
         c.ksplit = 5;
-        c.flags = ttable[layer][2].dma ? kFlagDma : 0;
+        c.flags = kFlagDma;
         return c;
     }
-    if (m > 256 && ne % 256 == 0) {
-        auto split_for = [](long tiles) { return (int)std::max(1L, std::min(4L, 256 / tiles)); };
-        const long t64 = (long)(ne / 256) * ((m + 63) / 64);
-        const long t128 = (long)(ne / 256) * ((m + 127) / 128);
-        int nt = 0;
-        long tiles = 0;
-        if (t64 <= 256 && t64 * split_for(t64) >= 160) {
-            nt = 4;
-            tiles = t64;
-        } else if (t128 * split_for(t128) <= (layer == PROJ_O ? 256 : 512)) {
-            nt = 8;
-            tiles = t128;
-        }
-        if (nt) {
+    // Past 256 tokens: 128 x 128 tiles on 4 waves while that fills the chip
+    // with at most 4 K splits (qkv_gate to 896 tokens, the other layers to
+    // 512), then 256 x 128 tiles on 8 waves (two per SIMD); the split count
+    // the largest that keeps the grid within 256 workgroups (the unpooler and
+    // o: no split), activations by LDS DMA where it measured faster; the
+    // pooler at 257-320 tokens on 256 x 64 tiles with 3 splits (3.7 us ahead
+    // of the 128 x 128 ones there). In-process cold A/B against the earlier
+    // rule (256 x 64 tiles on 8 waves while they gave 160 workgroups, else
+    // 256 x 128 within 512 workgroups, 256 for o, else 4-wave tiles; tuned
+    // with the non-temporal flush), us: qkv_gate m = 300 / 512 / 768 / 1500
+    // 33.7 / 40.6 / 53.8 / 87.5 -> 28.3 / 34.0 / 44.4 / 69.2; pooler m = 384 /
+    // 512 / 640 / 1000 51.2 / 51.7 / 82.0 / 85.4 -> 42.3 / 44.4 / 53.5 / 71.8;
+    // unpooler m = 300 / 512 44.4 / 47.0 -> 39.5 / 41.4; o m = 300 / 512 /
+    // 2048 14.7 / 15.9 / 55.5 -> 13.2 / 14.4 / 42.9; ties on the unpooler from
+    // 640 tokens up to 2048. Past 2048 tokens (cold sweep, m = 8192) o /
+    // unpooler / pooler / qkv_gate 227 / 653 / 608 / 372 -> 167 / 486 / 445 /
+    // 309 us, and equal where the earlier rule already chose these tiles.
+    if (m > 256) {
+        if (layer == PROJ_POOLER && m <= 320) {
             c.kind = 3;
             c.rb = 16;
-            c.nt = nt;
+            c.nt = 4;
             c.waves = 8;
             c.spw = 8;
-            int ks = split_for(tiles);
-            while (ks > 1 && tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes)
-                --ks;
-            c.ksplit = ks;
-            c.flags = ttable[layer][3].dma ? kFlagDma : 0;
+            c.ksplit = 3;
+            c.flags = kFlagDma;
             return c;
         }
+        struct Big {
+            int maxA, ksmax, dmaA, dmaB;      // last m on 128 x 128 tiles; split cap; DMA per family
+        };
+        static const Big big[PROJ_ROUTER] = {
+            /* qkv_gate */ {896, 4, 0, 0},
+            /* o        */ {512, 1, 1, 0},
+            /* pooler   */ {512, 4, 1, 1},
+            /* unpooler */ {512, 1, 1, 1},
+        };
+        const Big &b = big[layer];
+        const bool A = m <= b.maxA;
+        c.kind = 3;
+        c.nt = 8;
+        c.rb = A ? 8 : 16;
+        c.waves = A ? 4 : 8;
+        c.spw = 8;
+        const long tiles = (long)(ne / (16 * c.rb)) * ((m + 127) / 128);
+        int ks = (int)std::max(1L, std::min((long)b.ksmax, 256 / tiles));
+        while (ks > 1 && tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes)
+            --ks;
+        c.ksplit = ks;
+        c.flags = (A ? b.dmaA : b.dmaB) ? kFlagDma : 0;
+        return c;
     }
-    const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : (m <= 256 ? 2 : 3))];
+    const TEntry &e = ttable[layer][m <= 64 ? 0 : (m <= 128 ? 1 : 2)];
     c.kind = e.kind;
     c.rb = e.rb;
     c.nt = e.nt;
     c.waves = e.waves;
     c.spw = e.depth;
-    const long n_rt = ne / (16 * c.rb);
-    if (m > 256 && n_rt * ((m + 63) / 64) > 256) {
-        c.nt = 8;
-        c.spw = e.depth < 8 ? e.depth : 8;
-    }
-    const long tiles = n_rt * ((m + 16 * c.nt - 1) / (16 * c.nt));
+    const long tiles = (long)(ne / (16 * c.rb)) * ((m + 16 * c.nt - 1) / (16 * c.nt));
     int ks = e.ksplit > 0 ? e.ksplit : (int)std::max(1L, std::min(4L, 256 / tiles));
-    while (ks > 1 && (tiles * ks > 768 || tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes))
+    while (ks > 1 && tiles * ks * c.rb * c.nt * 1024 > (long)kWsBytes)
         ks = e.kind == 3 ? ks - 1 : ks / 2;   // the tiled kernel splits K into equal powers of two
     c.ksplit = ks;
     c.flags = (e.kind == 3 && e.dma) ? kFlagDma : 0;

@@ -130,8 +130,8 @@ int proj_run(int layer, const void *x, int m, void *out, void *stream);
  * interfere. A reducer give-up is counted for proj_split_giveups(layer), whose
  * reset also restores the array's marks.
  * Errors: those of proj_run, and PROJ_ERR_SCRATCH when (layer, m)'s plan needs
- * more partials or counters than the array holds (for instance the router past
- * 1024 tokens); nothing is launched then.
+ * more partials or counters than the array holds (for instance the pooler at
+ * 1000 tokens); nothing is launched then.
  */
 int proj_run_noalloc(int layer, const void *x, int m, void *out, void *stream);
 

@@ -126,7 +126,7 @@ def test_dispatch_plans_tile_every_layer(lib):
                 assert 1 <= cfg.ksplit <= k // (128 if cfg.spw >= 16 else 64)
                 # activations by LDS DMA (bit 7) where it measured faster; no other bit
                 dma = (name == "pooler" and m > 64) or (name == "unpooler" and m > 128) or \
-                      (name == "qkv_gate" and 128 < m <= 256)
+                      (name == "qkv_gate" and 128 < m <= 256) or (name == "o" and 256 < m <= 512)
                 assert cfg.flags == (128 if dma else 0)
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
@@ -169,15 +169,21 @@ def test_large_m_split_counts_keep_one_workgroup_per_cu(lib):
                 assert tiles * (cfg.ksplit + 1) > 256 or cfg.ksplit == 4, (name, m, cfg.as_dict())
 
 
-def test_router_past_8192_tokens_drops_the_split(lib):
-    # The polled split's partials grow with m; past 8192 tokens they would not
-    # fit the 32 MB workspace, so the plan keeps the whole K range in one
-    # workgroup (16 waves x 16 k-steps).
-    for m in (256, 4096, 8192):
-        assert binding.proj_plan("router", m).ksplit == 4, m
-    for m in (8193, 20000, 1 << 20):
+def test_router_plans_past_256_tokens(lib):
+    # Up to 256 tokens the skinny kernel with a 4-way polled split; past that
+    # the wide kernel's FP32 tiles (64 rows, 64 tokens up to 1024 and 128
+    # beyond) with a counted split of at most 8 whose partials fit the 32 MB
+    # workspace, down to no split where the tiles alone fill the chip.
+    assert binding.proj_plan("router", 256).as_dict()["kind"] == 0
+    assert binding.proj_plan("router", 256).ksplit == 4
+    for m in (257, 300, 512, 1000, 1024, 1025, 2048, 4096, 8192, 8193, 20000, 1 << 20):
         cfg = binding.proj_plan("router", m)
-        assert (cfg.kind, cfg.waves, cfg.spw, cfg.ksplit) == (0, 16, 16, 1), (m, cfg.as_dict())
+        nt = 4 if m <= 1024 else 8
+        assert (cfg.kind, cfg.nt, cfg.rb, cfg.waves, cfg.spw, cfg.flags) == (3, nt, 4, 4, 4, 0), (m, cfg.as_dict())
+        tiles = 4 * -(-m // (16 * nt))
+        assert 1 <= cfg.ksplit <= 8 and cfg.grid == tiles * cfg.ksplit
+        assert cfg.ksplit == 1 or tiles * cfg.ksplit * 64 * 16 * nt * 4 <= 32 << 20, (m, cfg.as_dict())
+    assert binding.proj_plan("router", 1 << 20).ksplit == 1
 
 
 def test_binding_rejects_bad_tensors_before_launch():

@@ -4,9 +4,11 @@ scratch in the library's fixed device array, called through the C ABI.
 Checked against proj_run on the same inputs (bit-identical: same kernels, same
 summation order) and against the oracle, for two calls in a row on one layer,
 the second with fewer tokens (the array keeps the first call's state), over
-plans with every kind of split-K scratch: polled partials (router, qkv_gate at
-32 tokens, qkv_gate's stream partition at 9-16 tokens), counted partials with
-arrival counters (wide-tile splits at 130, 200, 256 and 300 tokens), and none.
+plans with every kind of split-K scratch: polled partials (the router at 16-32
+tokens, the unpooler slice at 5, qkv_gate's stream partition at 9), counted
+partials with
+arrival counters (wide-tile splits: qkv_gate at 16-32 tokens, 130-256 tokens on
+the BF16 layers, the router's FP32 tiles at 300 and 1024 tokens), and none.
 """
 
 import numpy as np
@@ -61,18 +63,21 @@ def test_noalloc_matches_proj_run(layer, m1, m2):
 
 
 def test_noalloc_rejects_plans_beyond_its_scratch():
-    """The router's polled partials at 2048 tokens need 8 MiB, more than the
-    fixed array's 4 MiB: the call is refused on the host and launches nothing."""
-    _weights("router")
-    m = 2048
-    xd = to_device_x(make_x("router", m, seed=7).bits)
-    out = binding.new_out("router", m)
+    """The pooler's counted partials at 1000 tokens (256 x 128 tiles, 2 K
+    splits) need 32 MiB, more than the fixed array's 16 MiB for them: the call
+    is refused on the host and launches nothing."""
+    _weights("pooler")
+    m = 1000
+    cfg = binding.proj_plan("pooler", m)
+    assert (cfg.kind, cfg.rb, cfg.nt, cfg.ksplit) == (3, 16, 8, 2)
+    xd = to_device_x(make_x("pooler", m, seed=7).bits)
+    out = binding.new_out("pooler", m)
     out.fill_(float("nan"))
     with pytest.raises(binding.ProjError) as e:
-        binding.proj_run_noalloc("router", xd, m, out)
+        binding.proj_run_noalloc("pooler", xd, m, out)
     assert e.value.status == -9
     torch.cuda.synchronize()
-    assert torch.isnan(out).all()
-    binding.proj_run("router", xd, m, out)        # the allocating entry point still serves it
+    assert torch.isnan(out.float()).all()
+    binding.proj_run("pooler", xd, m, out)        # the allocating entry point still serves it
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
+    assert torch.isfinite(out.float()).all()
