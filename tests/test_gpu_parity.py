@@ -671,12 +671,17 @@ def test_bf16_output_rounding_is_nearest_even():
     _dirty()
 
 
-def test_router_keeps_fp32_weight_bits():
+@pytest.mark.parametrize("m", [1, 16, 256, 300, 1100, 2048])
+def test_router_keeps_fp32_weight_bits(m):
     """Router weights that BF16 cannot hold must still reach the sum exactly: a
-    probe row returns the FP32 weight column bit for bit."""
+    probe row returns the FP32 weight column bit for bit, on every router
+    kernel (row-dot at 1 token, the skinny kernel's three-part split at 16 and
+    256, the wide-tile kernel's at 300-2048)."""
     p = prepared(0)
-    xs = make_x("router", 1, seed=800, probe_variant=True)
+    xs = make_x("router", m, seed=800 + m, probe_variant=True)
+    say("router exact bits", binding.proj_plan("router", m).as_dict(), "m=%d" % m)
     got = run_layer("router", xs.bits)
-    (row, kk, e), = xs.probes
-    want = p.w["router"][:, kk].astype(np.float64) * 2.0 ** e
-    assert np.array_equal(got[row], want)
+    assert xs.probes
+    for row, kk, e in xs.probes:
+        want = p.w["router"][:, kk].astype(np.float64) * 2.0 ** e
+        assert np.array_equal(got[row], want), (m, row, kk)
