@@ -604,15 +604,17 @@ proj_config plan_default(int layer, int m, int zcr)
     // In-process cold A/B against register staging (us): pooler m = 128 /
     // 256 / 512 / 1000 24.8 / 32.9 / 53.9 / 88.9 -> 24.3 / 31.6 / 52.5 / 85.3;
     // unpooler m = 256 / 512 / 1000 30.7 / 47.7 / 62.5 -> 30.0 / 47.0 / 60.3;
-    // qkv_gate m = 256 25.7 -> 25.1. Elsewhere it tied or lost (o m = 256
-    // 11.3 -> 12.3, qkv_gate m = 128 19.0 -> 19.5).
+    // qkv_gate m = 256 25.7 -> 25.1. Elsewhere it tied or lost (qkv_gate
+    // m = 128 19.0 -> 19.5; o m = 256 11.3 -> 12.3 at prefetch depth 4). o at
+    // 129-256 tokens with depth 8 and DMA, against depth 4 without: m = 160 /
+    // 200 / 256 10.56 / 10.74 / 11.08 -> 9.80 / 9.90 / 10.40.
     struct TEntry {
         int kind, rb, nt, waves, depth, ksplit, dma;
     };
     // Measured in the same cold sweeps (m = 64, 128, 256).
     static const TEntry ttable[PROJ_ROUTER][3] = {   // the four BF16 layers
         /* qkv_gate */ {{3, 4, 4, 4, 16, 6, 0}, {3, 4, 4, 4, 16, 3, 0}, {3, 8, 4, 4, 16, 0, 1}},
-        /* o        */ {{1, 4, 2, 4, 16, 1, 0}, {1, 8, 2, 4, 8, 1, 0}, {3, 8, 4, 4, 4, 0, 0}},
+        /* o        */ {{1, 4, 2, 4, 16, 1, 0}, {1, 8, 2, 4, 8, 1, 0}, {3, 8, 4, 4, 8, 0, 1}},
         /* pooler   */ {{3, 4, 4, 4, 8, 4, 0}, {3, 8, 4, 4, 8, 4, 1}, {3, 8, 8, 8, 8, 0, 1}},
         /* unpooler */ {{1, 4, 2, 4, 16, 1, 0}, {3, 4, 4, 4, 16, 1, 0}, {3, 8, 4, 4, 16, 0, 1}},
     };

@@ -126,7 +126,7 @@ def test_dispatch_plans_tile_every_layer(lib):
                 assert 1 <= cfg.ksplit <= k // (128 if cfg.spw >= 16 else 64)
                 # activations by LDS DMA (bit 7) where it measured faster; no other bit
                 dma = (name == "pooler" and m > 64) or (name == "unpooler" and m > 128) or \
-                      (name == "qkv_gate" and 128 < m <= 256) or (name == "o" and 256 < m <= 512)
+                      (name == "qkv_gate" and 128 < m <= 256) or (name == "o" and 128 < m <= 512)
                 assert cfg.flags == (128 if dma else 0)
             assert ne % (16 * cfg.rb) == 0
             n_tt = -(-m // (16 * cfg.nt))
