@@ -622,13 +622,16 @@ proj_config plan_default(int layer, int m, int zcr)
     // The pooler at 129-192 tokens: 256 x 64 tiles on 8 waves with 5 splits
     // (240 workgroups) beat its 128 x 64 tiles with 2 (m = 130 / 160 / 192:
     // 24.6 / 24.9 / 25.6 -> 23.6 / 24.2 / 24.3 us); the other layers, and the
-    // pooler at 193-256, measured no gain.
+    // pooler at 193-256, measured no gain. A 16-k-step weight prefetch (four
+    // k-steps per activation super-step, one barrier per four k-steps) beat
+    // depth 8 on this tile: m = 130 / 144 / 160 / 176 / 192 30.00 / 30.00 /
+    // 30.48 / 30.70 / 30.94 -> 29.40 / 29.54 / 30.00 / 30.30 / 30.52 us.
     if (layer == PROJ_POOLER && m > 128 && m <= 192) {
         c.kind = 3;
         c.rb = 16;
         c.nt = 4;
         c.waves = 8;
-        c.spw = 8;
+        c.spw = 16;
         c.ksplit = 5;
         c.flags = kFlagDma;
         return c;

@@ -30,6 +30,7 @@ const WideVariant kWideDmaVariants[] = {
     GDP_WIDE_DMA(1, 8, 8, 8)
     GDP_WIDE_DMA(2, 4, 8, 8)
     GDP_WIDE_DMA(2, 8, 8, 8)
+    GDP_WIDE_DMA(2, 4, 16, 8)
 };
 const int kWideDmaVariantCount = sizeof(kWideDmaVariants) / sizeof(kWideDmaVariants[0]);
 
