@@ -37,6 +37,7 @@ const WideVariant kWideVariants[] = {
     GDP_WIDE_W(1, 4, 4, 0, 8)
     GDP_WIDE_W(1, 8, 8, 0, 8)
     GDP_WIDE_W(2, 4, 8, 0, 8)
+    GDP_WIDE_W(2, 4, 16, 0, 8)
     GDP_WIDE_W(2, 8, 8, 0, 8)
 };
 const int kWideVariantCount = sizeof(kWideVariants) / sizeof(kWideVariants[0]);
