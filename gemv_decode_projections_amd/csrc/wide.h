@@ -26,9 +26,12 @@
 //   * Activations are staged through a 4-slot LDS ring in super-steps of S
 //     k-steps: consecutive lanes read one token's contiguous S*64 bytes two
 //     super-steps ahead and write them where the MFMA B operand is read
-//     (lane l: token l%16, k = 8*(l/16)+0..7), rotated per token so that
-//     the reads of one 16-lane phase hit 16 distinct 16-byte bank groups.
-//     One barrier per super-step.
+//     (lane l: token l%16, k = 8*(l/16)+0..7): token q's four 16-byte
+//     k-groups fill units 4q..4q+3, rotated by q/2. That rotation reads
+//     without LDS bank conflicts on gfx950 (4 LDS cycles per 1 KB
+//     ds_read_b128, by the hardware's conflict counter); rotating by q/4,
+//     which spreads every 16-lane phase over 16 bank groups, measured 2-way
+//     conflicts (8 cycles). One barrier per super-step.
 //   * B fragments are double-buffered in registers: the next k-step's are
 //     read from LDS one at a time between the current k-step's MFMAs
 //     (explicit scheduling groups; at one wave per SIMD nothing else hides
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(WAVES * kWave) void wide_kernel(WideArgs a)
     const uint16_t *xsrc[XPT];
     int xdst[XPT];
     // XDMA: lane l of a block fills LDS unit l of that block, i.e. token l/4,
-    // k-group ((l % 4) - l/16) & 3 (the inverse of the rotation above), so
+    // k-group ((l % 4) - l/8) & 3 (the inverse of the rotation above), so
     // each lane quad still reads one token's contiguous 64 bytes.
     const uint16_t *dsrc[XDMA ? NB : 1];
     int ddst[XDMA ? NB : 1];
@@ -187,10 +190,10 @@ __global__ __launch_bounds__(WAVES * kWave) void wide_kernel(WideArgs a)
             const int sub = c / 4, g = c % 4;
             const int tok = tok0 + qt;
             xsrc[i] = (tok < a.m ? a.x + (size_t)tok * a.K : a.zrow) + 8 * c;
-            xdst[i] = sub * REG + blk * kWave + 4 * q + ((g + q / 4) & 3);
+            xdst[i] = sub * REG + blk * kWave + 4 * q + ((g + q / 2) & 3);
         }
         if constexpr (XDMA) {
-            const int q = lane / 4, g = ((lane % 4) - q / 4) & 3;
+            const int q = lane / 4, g = ((lane % 4) - q / 2) & 3;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int blk = wave * NB + b, sub = blk / BNB, t = blk % BNB;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(WAVES * kWave) void wide_kernel(WideArgs a)
         }
     };
     // LDS unit holding (token l%16, k-group l/16) of a fragment for this lane.
-    const int bslot = 4 * (lane % 16) + (((lane / 16) + (lane % 16) / 4) & 3);
+    const int bslot = 4 * (lane % 16) + (((lane / 16) + (lane % 16) / 2) & 3);
 
     f32x4 acc[RBW][BNB];
 
