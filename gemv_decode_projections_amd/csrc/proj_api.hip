@@ -626,6 +626,24 @@ proj_config plan_default(int layer, int m, int zcr)
     // k-steps per activation super-step, one barrier per four k-steps) beat
     // depth 8 on this tile: m = 130 / 144 / 160 / 176 / 192 30.00 / 30.00 /
     // 30.48 / 30.70 / 30.94 -> 29.40 / 29.54 / 30.00 / 30.30 / 30.52 us.
+    // The unpooler at 129-256 tokens: its 64-token tiles without a split
+    // take longer the fuller their last tile, 128 x 128 tiles with 2 splits
+    // (256 workgroups) stay near 28.5 us, so the latter once the last
+    // 64-token tile holds more than 32 tokens (cold A/B, plan -> 128 x 128,
+    // us: m = 168 / 176 / 184 / 192 28.98 / 29.42 / 29.48 / 29.68 -> 28.40
+    // / 28.56 / 28.58 / 28.48; m = 232 / 240 / 248 / 256 29.08 / 29.24 /
+    // 29.72 / 29.52 -> 28.36 / 28.44 / 28.64 / 29.00; with fewer in the
+    // last tile a tie or a loss: m = 136 / 200 / 208 +0.62 / +0.36 / +0.18).
+    if (layer == PROJ_UNPOOLER && m > 128 && m <= 256 && (m - 1) % 64 >= 32) {
+        c.kind = 3;
+        c.rb = 8;
+        c.nt = 8;
+        c.waves = 4;
+        c.spw = 8;
+        c.ksplit = 2;
+        c.flags = kFlagDma;
+        return c;
+    }
     if (layer == PROJ_POOLER && m > 128 && m <= 192) {
         c.kind = 3;
         c.rb = 16;
