@@ -477,6 +477,8 @@ PMC_CMDS = (
     "-- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_write.log 2>&1",
     "cd /tmp && rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d $OUT/pmc_mfma "
     "-o mfma -- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_mfma.log 2>&1",
+    "cd /tmp && rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE --output-format csv -d $OUT/pmc_lds "
+    "-o lds -- python3 $REPO/bench.py --pmc-pass > $OUT/pmc_lds.log 2>&1",
 )
 PMC_HASH_TAG = "pmc pass kernel sources:"
 
@@ -553,7 +555,7 @@ def md_graph_trace(gt, trace_csv, graph_reps):
 def md_pmc(pm, csvs, logs):
     """profiles/pmc_loads.md from summarize_pmc()'s result."""
     args = "%s --pmc-logs %s" % (" ".join(shown(c) for c in csvs), " ".join(shown(g) for g in logs))
-    L = ["# HBM traffic and MFMA use per launch, every load: rocprofv3 --pmc (MI355X, 1 GPU)", "",
+    L = ["# HBM traffic, MFMA use and LDS bank conflicts per launch, every load: rocprofv3 --pmc (MI355X, 1 GPU)", "",
          "Commands (%s; one counter set per run):" % CMD_VARS, "", "```"] + list(PMC_CMDS) + [
          "python bench.py --summarize-pmc %s > profiles/pmc_loads.json" % args,
          "python bench.py --summarize-pmc %s --md > profiles/pmc_loads.md" % args, "```", "",
@@ -563,18 +565,20 @@ def md_pmc(pm, csvs, logs):
          % (pm["fetch_scale"], pm["write_scale"]),
          "are multiplied by their scale. Medians of the %d passes. MFMA util = MFMA-busy cycles over all SIMD cycles"
          % PMC_REPS,
-         "of the dispatch (rocprofv3's MfmaUtil); MOPS = SQ_INSTS_VALU_MFMA_MOPS_BF16 as counted. Kernels whose last",
+         "of the dispatch (rocprofv3's MfmaUtil); MOPS = SQ_INSTS_VALU_MFMA_MOPS_BF16 as counted. LDS conflict % =",
+         "SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE: the share of the LDS's indexed-access cycles lost to bank",
+         "conflicts (0 when every access is conflict-free; 50 when each one takes twice its cycles). Kernels whose last",
          "template argument is `true` read 12-bit lossless weights (3/4 of the BF16 bytes plus a correction table).",
          "FETCH_SIZE counts what the L2 caches fetch from memory (HBM or the Infinity Cache behind them); each XCD's",
          "L2 fetches its own copy of data that workgroups on several XCDs read (x at large m).", "",
          "| load | layer | kernel | fetched by L2 (FETCH_SIZE, bytes) | written (WRITE_SIZE, bytes) | algorithmic bytes "
-         "| traffic / algorithmic | MFMA util % | MFMA MOPS (bf16) |",
-         "|---|---|---|---|---|---|---|---|---|"]
+         "| traffic / algorithmic | MFMA util % | MFMA MOPS (bf16) | LDS conflict % |",
+         "|---|---|---|---|---|---|---|---|---|---|"]
     for key, e in pm["launches"].items():
-        L.append("| %s | %s | `%s` | %d | %d | %d | %.3f | %s | %s |" % (
+        L.append("| %s | %s | `%s` | %d | %d | %d | %.3f | %s | %s | %s |" % (
             e["load"], key.split("@")[0], e["kernel"], e["fetch_bytes"], e["write_bytes"], e["algorithmic_bytes"],
             (e["fetch_bytes"] + e["write_bytes"]) / e["algorithmic_bytes"], e.get("mfma_util_pct", "-"),
-            e.get("mfma_mops_bf16", "-")))
+            e.get("mfma_mops_bf16", "-"), e.get("lds_conflict_pct", "-")))
     L += ["", "Source hash of the kernels these counters belong to, as printed by the passes themselves: `%s` "
           "(bench.py reports `traffic` = null once the sources differ)." % pm["source_hash"], ""]
     return "\n".join(L)
@@ -624,14 +628,16 @@ def pass_source_hash(logs):
     return seen.pop()
 
 
-def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20, sources=None):
+def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, lds_csv=None, copy_bytes=64 << 20, sources=None):
     """HBM bytes (and MFMA use) per launch of every (load, layer) from the counter
     passes of `bench.py --pmc-pass`.
 
     FETCH_SIZE and WRITE_SIZE are scaled by what they read on the copy kernel
     of known size in the same pass (copy_bytes read and copy_bytes written).
     The optional third pass holds MfmaUtil (MFMA-busy cycles over all SIMD
-    cycles of the dispatch, percent) and SQ_INSTS_VALU_MFMA_MOPS_BF16.
+    cycles of the dispatch, percent) and SQ_INSTS_VALU_MFMA_MOPS_BF16; the
+    optional fourth SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE (their ratio per
+    launch, percent; "-" where a launch makes no indexed LDS access).
     `sources`: the kernel-source hash the passes ran (pass_source_hash).
     """
     from gemv_decode_projections_amd import roofline as rf
@@ -677,6 +683,18 @@ def summarize_pmc(fetch_csv, write_csv, mfma_csv=None, copy_bytes=64 << 20, sour
                 vals.setdefault((name, layer), []).append(float(r["Counter_Value"]))
             for (name, layer), v in vals.items():
                 entry(name, layer)[key] = round(statistics.median(v), 2)
+    if lds_csv:
+        got = {}
+        for cname in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
+            _, sk = launches(lds_csv, cname)
+            got[cname] = [float(r["Counter_Value"]) for r in sk]
+        vals = {}
+        for i, (name, layer) in enumerate(seq):
+            act = got["SQ_LDS_IDX_ACTIVE"][i]
+            if act > 0:
+                vals.setdefault((name, layer), []).append(100.0 * got["SQ_LDS_BANK_CONFLICT"][i] / act)
+        for (name, layer), v in vals.items():
+            entry(name, layer)["lds_conflict_pct"] = round(statistics.median(v), 1)
     return res
 
 
@@ -907,7 +925,7 @@ def main():
                     help="with --summarize-pmc: the passes' output (names the kernel sources they ran)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="print HBM bytes per launch from the --pmc passes: FETCH_SIZE csv, WRITE_SIZE csv "
-                         "and optionally the MfmaUtil csv")
+                         "and optionally the MfmaUtil csv and the LDS bank-conflict csv")
     args = ap.parse_args()
     global OUT_ROOT
     OUT_ROOT = args.out_root
@@ -933,8 +951,8 @@ def main():
         print(md_flush_study(last_line(args.flush_study_md), args.flush_study_md))
         return
     if args.summarize_pmc:
-        if len(args.summarize_pmc) not in (2, 3):
-            raise SystemExit("--summarize-pmc takes FETCH_CSV WRITE_CSV [MFMA_CSV]")
+        if len(args.summarize_pmc) not in (2, 3, 4):
+            raise SystemExit("--summarize-pmc takes FETCH_CSV WRITE_CSV [MFMA_CSV [LDS_CSV]]")
         if not args.pmc_logs:
             raise SystemExit("--summarize-pmc needs --pmc-logs (the passes' output, which names their sources)")
         pm = summarize_pmc(*args.summarize_pmc, sources=pass_source_hash(args.pmc_logs))

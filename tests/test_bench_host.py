@@ -65,8 +65,11 @@ def test_pmc_summary_scales_by_the_copy_and_keys_every_shape(tmp_path):
     _pmc_csv(tmp_path / "w.csv", ["WRITE_SIZE"], lambda n, l, c: 8.0, 64 << 10)
     _pmc_csv(tmp_path / "m.csv", ["MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_BF16"],
              lambda n, l, c: 12.5 if c == "MfmaUtil" else LOADS[n])
+    # LDS pass: conflicts on half the active cycles except the router's launches (no indexed LDS use)
+    _pmc_csv(tmp_path / "l.csv", ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"],
+             lambda n, l, c: 0.0 if l == "router" else (50.0 if c == "SQ_LDS_BANK_CONFLICT" else 100.0))
     r = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "m.csv"),
-                            sources="abc")
+                            str(tmp_path / "l.csv"), sources="abc")
     assert r["fetch_scale"] == pytest.approx(2.0) and r["write_scale"] == pytest.approx(1.0)
     assert len(r["launches"]) == len(LOADS) * len(LAYERS)
     for name, m in LOADS.items():
@@ -77,6 +80,7 @@ def test_pmc_summary_scales_by_the_copy_and_keys_every_shape(tmp_path):
             assert e["write_bytes"] == 8192
             assert e["algorithmic_bytes"] == rf.bytes_of(layer, m)
             assert e["mfma_util_pct"] == 12.5 and e["mfma_mops_bf16"] == m
+            assert e.get("lds_conflict_pct") == (None if layer == "router" else 50.0)
     assert r["source_hash"] == "abc"
 
 
