@@ -169,6 +169,21 @@ def test_large_m_split_counts_keep_one_workgroup_per_cu(lib):
                 assert tiles * (cfg.ksplit + 1) > 256 or cfg.ksplit == 4, (name, m, cfg.as_dict())
 
 
+def test_wide_plans_between_129_and_256_tokens(lib):
+    # The pooler at 129-192 tokens: 256 x 64 tiles on 8 waves, a 16-k-step prefetch, 5 splits.
+    # The unpooler: 128 x 64 tiles without a split, or 128 x 128 tiles with 2 splits once the
+    # last 64-token tile holds more than 32 tokens.
+    for m in range(129, 257):
+        p = binding.proj_plan("pooler", m)
+        if m <= 192:
+            assert (p.kind, p.rb, p.nt, p.waves, p.spw, p.ksplit, p.flags) == (3, 16, 4, 8, 16, 5, 128), m
+        u = binding.proj_plan("unpooler", m)
+        big = (m - 1) % 64 >= 32
+        assert (u.kind, u.rb, u.nt, u.waves, u.ksplit, u.flags) == \
+            ((3, 8, 8, 4, 2, 128) if big else (3, 8, 4, 4, 1, 128)), (m, u.as_dict())
+        assert u.grid == (256 if big else 64 * -(-m // 64)), (m, u.as_dict())
+
+
 def test_router_plans_past_256_tokens(lib):
     # Up to 256 tokens the skinny kernel with a 4-way polled split; past that
     # the wide kernel's FP32 tiles (64 rows, 64 tokens up to 1024 and 128

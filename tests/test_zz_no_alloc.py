@@ -8,7 +8,8 @@ plans with every kind of split-K scratch: polled partials (the router at 16-32
 tokens, the unpooler slice at 5, qkv_gate's stream partition at 9), counted
 partials with
 arrival counters (wide-tile splits: qkv_gate at 16-32 tokens, 130-256 tokens on
-the BF16 layers, the router's FP32 tiles at 300 and 1024 tokens), and none.
+the BF16 layers, the router's FP32 tiles at 300 and 1024 tokens, the unpooler's 128 x 128 tiles at 256 tokens,
+whose 16 MiB of partials fill the array's counted region exactly), and none.
 """
 
 import numpy as np
@@ -45,7 +46,8 @@ def _run(fn, layer, xd, m):
 
 @pytest.mark.parametrize("layer,m1,m2", [("router", 32, 16), ("qkv_gate", 32, 17), ("qkv_gate", 16, 9),
                                          ("pooler", 256, 130), ("qkv_gate", 256, 200), ("o", 300, 64),
-                                         ("unpooler", 9, 5), ("router", 1024, 300)])
+                                         ("unpooler", 9, 5), ("router", 1024, 300),
+                                         ("unpooler", 256, 200)])
 def test_noalloc_matches_proj_run(layer, m1, m2):
     w = _weights(layer)
     for m in (m1, m2):
